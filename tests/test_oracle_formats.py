@@ -1,0 +1,147 @@
+"""Pins of the oracle's element and scale codecs against closed forms and
+torch's CPU float8 codecs (library routines independent of the oracle)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import formats as F
+from oracle.brute import e2m1_closed_form
+
+
+def test_e2m1_table_matches_closed_form():
+    codes = np.arange(16, dtype=np.uint8)
+    table = F.e2m1_value(codes)
+    closed = np.array([e2m1_closed_form(int(c)) for c in codes])
+    np.testing.assert_array_equal(table, closed)
+    # sign bit 3; code 8 is negative zero
+    assert table[8] == 0.0 and np.signbit(table[8])
+    np.testing.assert_array_equal(table[8:], -table[:8])
+    np.testing.assert_array_equal(table[:8], [0, 0.5, 1, 1.5, 2, 3, 4, 6])
+
+
+def test_nibble_round_trip_all_bytes():
+    b = np.arange(256, dtype=np.uint8).reshape(16, 16)
+    c = F.unpack_nibbles(b)
+    assert c.shape == (16, 32)
+    np.testing.assert_array_equal(F.pack_nibbles(c), b)
+    # element 2j from the low nibble (the reading used throughout)
+    np.testing.assert_array_equal(F.unpack_nibbles(np.array([0x21], np.uint8)), [1, 2])
+    rng = np.random.default_rng(0)
+    r = rng.integers(0, 256, size=(7, 40), dtype=np.uint8)
+    np.testing.assert_array_equal(F.pack_nibbles(F.unpack_nibbles(r)), r)
+
+
+def test_pack_rejects_bad_codes():
+    with pytest.raises(ValueError):
+        F.pack_nibbles(np.array([16, 0], np.uint8))
+    with pytest.raises(ValueError):
+        F.pack_nibbles(np.array([1, 2, 3], np.uint8))
+
+
+def test_e8m0_closed_form_and_torch():
+    b = np.arange(256, dtype=np.uint8)
+    v = F.e8m0_value(b)
+    t = torch.from_numpy(b.copy()).view(torch.float8_e8m0fnu).to(torch.float64).numpy()
+    np.testing.assert_array_equal(v[:255], t[:255])
+    assert np.isnan(v[255]) and np.isnan(t[255])
+    for k in range(255):
+        assert v[k] == 2.0 ** (k - 127)
+    # bf16 exponent-field expansion (byte << 7) is exact for 1..254
+    bits = (np.arange(1, 255, dtype=np.uint16) << 7)
+    np.testing.assert_array_equal(F.bf16_bits_to_f64(bits), v[1:255])
+
+
+def test_scale_validation_names_first_bad_byte():
+    s = np.full((3, 4), 127, np.uint8)
+    F.validate_scale_bytes(s)
+    s[1, 2] = 0xFF
+    with pytest.raises(ValueError, match=r"0xFF at index \(1, 2\)"):
+        F.validate_scale_bytes(s)
+    s[1, 2] = 0x00
+    with pytest.raises(ValueError, match="0x00"):
+        F.validate_scale_bytes(s)
+
+
+def test_dequant_matches_scalar_decode():
+    rng = np.random.default_rng(1)
+    codes = rng.integers(0, 256, size=(5, 64 // 2), dtype=np.uint8)
+    scales = rng.integers(100, 150, size=(5, 2), dtype=np.uint8)
+    w = F.dequant_mxfp4(codes, scales)
+    for n in range(5):
+        for k in range(64):
+            byte = int(codes[n, k // 2])
+            code = (byte >> 4) if k % 2 else (byte & 15)
+            assert w[n, k] == e2m1_closed_form(code) * 2.0 ** (int(scales[n, k // 32]) - 127)
+
+
+def test_dequant_rejects_edge_scale_bytes():
+    codes = np.zeros((1, 16), np.uint8)
+    with pytest.raises(ValueError):
+        F.dequant_mxfp4(codes, np.array([[255]], np.uint8))
+    with pytest.raises(ValueError):
+        F.dequant_mxfp4(codes, np.array([[0]], np.uint8))
+
+
+def test_e4m3_decode_all_codes_vs_torch():
+    c = np.arange(256, dtype=np.uint8)
+    v = F.e4m3_value(c)
+    t = torch.from_numpy(c.copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    nan = np.isnan(t)
+    np.testing.assert_array_equal(np.isnan(v), nan)
+    np.testing.assert_array_equal(v[~nan], t[~nan])
+    assert nan.sum() == 2 and F.e4m3_value(np.array([0x7E]))[0] == 448.0
+
+
+def test_e4m3_encode_round_trips_every_finite_code():
+    c = np.array([i for i in range(256) if (i & 0x7F) != 0x7F], np.uint8)
+    np.testing.assert_array_equal(F.e4m3_encode(F.e4m3_value(c)), c)
+
+
+def test_e4m3_encode_vs_torch_cast():
+    rng = np.random.default_rng(2)
+    mags = np.ldexp(rng.random(200000) + 0.5, rng.integers(-14, 10, size=200000))
+    vals = np.where(rng.random(200000) < 0.5, -mags, mags).astype(np.float32)
+    clamped = np.clip(vals, -448.0, 448.0)
+    t = torch.from_numpy(clamped).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    np.testing.assert_array_equal(F.e4m3_encode(vals.astype(np.float64)), t)
+
+
+@pytest.mark.parametrize("v,code", [
+    (464.0, 0x7E),          # saturates to 448
+    (1e6, 0x7E),
+    (-1e6, 0xFE),
+    (2.0 ** -10, 0x00),     # tie between 0 and 2^-9 -> even (0)
+    (3 * 2.0 ** -11, 0x01),  # 0.75 of the subnormal step -> 2^-9
+    (17.0, 0x58),           # tie between 16 and 18 -> even mantissa (16)
+    (19.0, 0x5A),           # tie between 18 and 20 -> 20 (mantissa 2)
+    (-2.0 ** -11, 0x80),    # rounds to -0
+    (2.0 ** -6, 0x08),      # smallest normal
+    (15 * 2.0 ** -10, 0x08),  # rounds up from the subnormals into the normals
+])
+def test_e4m3_encode_special_values(v, code):
+    assert int(F.e4m3_encode(np.array([v]))[0]) == code
+
+
+def test_bf16_rne_vs_torch():
+    rng = np.random.default_rng(3)
+    a = np.concatenate([
+        rng.standard_normal(100000).astype(np.float32) * np.float32(1e3),
+        np.ldexp(rng.random(1000), rng.integers(-140, -120, 1000)).astype(np.float32),
+        np.array([0.0, -0.0, np.inf, -np.inf, 3.3895314e38, 1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8],
+                 np.float32),
+    ])
+    t = torch.from_numpy(a).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(F.f32_to_bf16_rne(a), t)
+    assert np.isnan(F.bf16_bits_to_f64(F.f32_to_bf16_rne(np.array([np.nan], np.float32))))[0]
+
+
+def test_ulp_bf16_values():
+    np.testing.assert_array_equal(
+        F.ulp_bf16(np.array([1.0, 1.5, 2.0, -3.0, 0.0, 1e-45, 2.0 ** -126])),
+        [2.0 ** -7, 2.0 ** -7, 2.0 ** -6, 2.0 ** -6, 2.0 ** -133, 2.0 ** -133, 2.0 ** -133])
+
+
+def test_oracle_package_exports():
+    for name in ("forward", "route_sort", "check_rows", "mxfp8_quantize", "dequant_mxfp4"):
+        assert hasattr(oracle, name)
