@@ -1,0 +1,185 @@
+"""Python binding of libmoe_mxfp4.so: the routed-expert MXFP4 MoE layer on
+AMD MI355X (gfx950).
+
+Argument marshalling only: every step of the layer runs in the HIP library.
+torch provides device memory and the current stream.  If the library has not
+been built, importing the low-level entry points raises at once; there is no
+other execution path.
+
+Names follow the C ABI in include/moe_mxfp4.h:
+  query_sizes(cfg)                      -> (repacked_bytes, workspace_bytes)
+  Plan(cfg, w13_codes, w13_scales, w2_codes, w2_scales)     (moe_mxfp4_plan)
+  Plan.forward(hidden, topk_ids, topk_weights, out=None, acc=None)
+  Plan.route(topk_ids)                  -> (counts, offsets, perm, rowpos)
+  mxfp8_quantize(x_bf16)                -> (codes, scales)
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+from typing import Optional
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmoe_mxfp4.so")
+
+MOE_ACT_BF16 = 0
+MOE_ACT_MXFP8 = 1
+STATUS_NAMES = {0: "MOE_OK", 1: "MOE_ERR_ARG", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_ALIGN", 4: "MOE_ERR_CAPACITY",
+                5: "MOE_ERR_SCALE_BYTE", 6: "MOE_ERR_WORKSPACE", 7: "MOE_ERR_UNSUPPORTED", 8: "MOE_ERR_HIP"}
+EXPORTS = ("moe_mxfp4_query_sizes", "moe_mxfp4_plan", "moe_mxfp4_forward", "moe_mxfp4_route",
+           "moe_mxfp8_quantize", "moe_mxfp4_set_stage_events", "moe_mxfp4_destroy", "moe_mxfp4_last_error")
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+        self.message = message
+
+
+class _Config(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_int32), ("intermediate", ctypes.c_int32), ("num_experts", ctypes.c_int32),
+                ("top_k", ctypes.c_int32), ("max_tokens", ctypes.c_int32), ("act", ctypes.c_int32)]
+
+
+@dataclasses.dataclass(frozen=True)
+class Config:
+    hidden: int
+    intermediate: int
+    num_experts: int
+    top_k: int
+    max_tokens: int
+    act: int = MOE_ACT_BF16
+
+    def c(self) -> _Config:
+        return _Config(self.hidden, self.intermediate, self.num_experts, self.top_k, self.max_tokens, self.act)
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load the HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"libmoe_mxfp4.so not found at {path}; build it with "
+                          f"`python -m mxfp4_routed_expert_topk_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    cfgp = ctypes.POINTER(_Config)
+    lib.moe_mxfp4_query_sizes.argtypes = [cfgp, ctypes.POINTER(sz), ctypes.POINTER(sz)]
+    lib.moe_mxfp4_plan.argtypes = [cfgp, vp, vp, vp, vp, vp, sz, vp, ctypes.POINTER(vp)]
+    lib.moe_mxfp4_forward.argtypes = [vp, vp, vp, vp, i32, vp, vp, vp, sz, vp]
+    lib.moe_mxfp4_route.argtypes = [vp, vp, i32, vp, vp, vp, vp, vp, sz, vp]
+    lib.moe_mxfp8_quantize.argtypes = [vp, i32, i32, vp, vp, vp]
+    lib.moe_mxfp4_set_stage_events.argtypes = [vp, ctypes.POINTER(vp), i32]
+    lib.moe_mxfp4_destroy.argtypes = [vp]
+    lib.moe_mxfp4_destroy.restype = None
+    lib.moe_mxfp4_last_error.argtypes = []
+    lib.moe_mxfp4_last_error.restype = ctypes.c_char_p
+    for name in ("moe_mxfp4_query_sizes", "moe_mxfp4_plan", "moe_mxfp4_forward", "moe_mxfp4_route",
+                 "moe_mxfp8_quantize", "moe_mxfp4_set_stage_events"):
+        getattr(lib, name).restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise MoeError(status, load_library().moe_mxfp4_last_error().decode())
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream=None) -> int:
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def query_sizes(cfg: Config):
+    lib = load_library()
+    rb, wb = ctypes.c_size_t(), ctypes.c_size_t()
+    _check(lib.moe_mxfp4_query_sizes(ctypes.byref(cfg.c()), ctypes.byref(rb), ctypes.byref(wb)))
+    return rb.value, wb.value
+
+
+class Plan:
+    """A plan over repacked weights.  Holds the repacked buffer and the
+    forward workspace as torch uint8 tensors on the current device."""
+
+    def __init__(self, cfg: Config, w13_codes, w13_scales, w2_codes, w2_scales, stream=None):
+        import torch
+        lib = load_library()
+        self.cfg = cfg
+        self.repacked_bytes, self.workspace_bytes = query_sizes(cfg)
+        dev = w13_codes.device
+        self.repacked = torch.empty(self.repacked_bytes, dtype=torch.uint8, device=dev)
+        self.workspace = torch.empty(self.workspace_bytes, dtype=torch.uint8, device=dev)
+        h = ctypes.c_void_p()
+        _check(lib.moe_mxfp4_plan(ctypes.byref(cfg.c()), _ptr(w13_codes), _ptr(w13_scales), _ptr(w2_codes),
+                                  _ptr(w2_scales), _ptr(self.repacked), self.repacked_bytes, _stream(stream),
+                                  ctypes.byref(h)))
+        self._h = h
+        self._events = None
+
+    def close(self):
+        if getattr(self, "_h", None) and self._h.value:
+            load_library().moe_mxfp4_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def forward(self, hidden, topk_ids, topk_weights, out=None, acc=None, num_tokens=None, stream=None,
+                workspace=None):
+        import torch
+        T = hidden.shape[0] if num_tokens is None else int(num_tokens)
+        if out is None:
+            out = torch.empty((hidden.shape[0], self.cfg.hidden), dtype=torch.bfloat16, device=hidden.device)
+        ws = self.workspace if workspace is None else workspace
+        _check(load_library().moe_mxfp4_forward(self._h, _ptr(hidden), _ptr(topk_ids), _ptr(topk_weights), T,
+                                                _ptr(acc), _ptr(out), _ptr(ws), ws.numel(), _stream(stream)))
+        return out
+
+    def route(self, topk_ids, num_tokens=None, stream=None):
+        import torch
+        T = topk_ids.shape[0] if num_tokens is None else int(num_tokens)
+        dev = topk_ids.device
+        E, n = self.cfg.num_experts, max(1, T * self.cfg.top_k)
+        counts = torch.empty(E, dtype=torch.int32, device=dev)
+        offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+        perm = torch.full((n,), -7, dtype=torch.int32, device=dev)
+        rowpos = torch.empty(n, dtype=torch.int32, device=dev)
+        _check(load_library().moe_mxfp4_route(self._h, _ptr(topk_ids), T, _ptr(counts), _ptr(offsets), _ptr(perm),
+                                              _ptr(rowpos), _ptr(self.workspace), self.workspace.numel(),
+                                              _stream(stream)))
+        return counts, offsets, perm, rowpos
+
+    def set_stage_events(self, events):
+        """events: list of 5 torch.cuda.Event(enable_timing=True) or None to stop."""
+        lib = load_library()
+        if not events:
+            _check(lib.moe_mxfp4_set_stage_events(self._h, None, 0))
+            self._events = None
+            return
+        arr = (ctypes.c_void_p * len(events))(*[ev.cuda_event for ev in events])
+        self._events = (events, arr)   # keep alive while set
+        _check(lib.moe_mxfp4_set_stage_events(self._h, arr, len(events)))
+
+
+def mxfp8_quantize(x_bf16, stream=None):
+    import torch
+    rows, cols = x_bf16.shape
+    codes = torch.empty((rows, cols), dtype=torch.uint8, device=x_bf16.device)
+    scales = torch.empty((rows, cols // 32), dtype=torch.uint8, device=x_bf16.device)
+    _check(load_library().moe_mxfp8_quantize(_ptr(x_bf16), rows, cols, _ptr(codes), _ptr(scales), _stream(stream)))
+    return codes, scales

@@ -1,0 +1,53 @@
+// Gather-weight-reduce epilogue: for every token t,
+//   acc_t = sum over slots s = 0..k-1 (ascending) with a valid route of
+//           w[t,s] * y[row(t,s)]      (fp32, fused multiply-add per term)
+//   out_t = RNE_bf16(acc_t)
+// Each output element is owned by one thread, so there are no atomics and the
+// order is fixed (pegainfer PR #867, commit 53edfa98: "topk-slot-order f32
+// accumulation, no atomics, single bf16 round").  The fp32 accumulator, when
+// the caller passes one, is overwritten in full and rounded once (b12x PR
+// #339: caller-owned fp32 token accumulator cast once; commit "top-k sum
+// output store element": the bf16 store rounds the same fp32 value once, to
+// nearest even).  Invalid routes are skipped, their weights never read.
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int kThreads = 256;
+
+__global__ __launch_bounds__(kThreads) void combine(const float* __restrict__ y, const int32_t* __restrict__ rowpos,
+                                                    const float* __restrict__ w, int k, int H,
+                                                    float* __restrict__ acc_out, uint16_t* __restrict__ out) {
+  const int t = blockIdx.x;
+  const int c = (blockIdx.y * kThreads + threadIdx.x) * 4;
+  if (c >= H) return;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int s = 0; s < k; ++s) {
+    const int r = rowpos[(size_t)t * k + s];
+    if (r < 0) continue;
+    const float ws = w[(size_t)t * k + s];
+    const float4 v = *reinterpret_cast<const float4*>(y + (size_t)r * H + c);
+    acc.x = fmaf(ws, v.x, acc.x);
+    acc.y = fmaf(ws, v.y, acc.y);
+    acc.z = fmaf(ws, v.z, acc.z);
+    acc.w = fmaf(ws, v.w, acc.w);
+  }
+  if (acc_out) *reinterpret_cast<float4*>(acc_out + (size_t)t * H + c) = acc;
+  const uint32_t lo = f32_to_bf16_rne(acc.x) | ((uint32_t)f32_to_bf16_rne(acc.y) << 16);
+  const uint32_t hi = f32_to_bf16_rne(acc.z) | ((uint32_t)f32_to_bf16_rne(acc.w) << 16);
+  *reinterpret_cast<uint2*>(out + (size_t)t * H + c) = make_uint2(lo, hi);
+}
+
+}  // namespace
+
+hipError_t launch_combine(const float* y, const int32_t* rowpos, const int32_t* /*ids*/,
+                          const float* w, int32_t T, int32_t k, int32_t H, int32_t /*E*/,
+                          float* acc, uint16_t* out, hipStream_t stream) {
+  if (T == 0) return hipSuccess;
+  const dim3 grid(T, (H / 4 + kThreads - 1) / kThreads);
+  hipLaunchKernelGGL(combine, grid, dim3(kThreads), 0, stream, y, rowpos, w, k, H, acc, out);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,352 @@
+// C ABI of the MXFP4 routed-expert MoE library: argument validation, buffer
+// layout, plan (repack + scale validation) and the forward launch sequence.
+//
+// Contract conventions follow the pages' hard-fail seams: every violation
+// returns an error that names what was expected and what was passed, with no
+// fallback path (batchgen PR #307: "every contract violation raises";
+// "error names the extension file actually loaded"); forward allocates
+// nothing and never writes its inputs (b12x PR #339, commit "FC2-only route
+// validation": no caller-tensor mutation, no allocation during graph replay).
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/moe_mxfp4.h"
+#include "moe_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+moe_status fail(moe_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+moe_status ok() {
+  g_err.clear();
+  return MOE_OK;
+}
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
+constexpr int32_t kMaxDim = 16384;
+constexpr int32_t kMaxExperts = 1024;
+constexpr int32_t kMaxTopK = 32;
+constexpr int64_t kMaxRoutes = 262144;
+
+moe_status check_config(const moe_mxfp4_config* c) {
+  if (!c) return fail(MOE_ERR_ARG, "config pointer is null");
+  if (c->hidden < 128 || c->hidden > kMaxDim || c->hidden % 128)
+    return fail(MOE_ERR_SHAPE, "hidden must be a multiple of 128 in [128, %d], got %d", kMaxDim, c->hidden);
+  if (c->intermediate < 128 || c->intermediate > kMaxDim || c->intermediate % 128)
+    return fail(MOE_ERR_SHAPE, "intermediate must be a multiple of 128 in [128, %d], got %d", kMaxDim,
+                c->intermediate);
+  if (c->num_experts < 1 || c->num_experts > kMaxExperts)
+    return fail(MOE_ERR_SHAPE, "num_experts must be in [1, %d], got %d", kMaxExperts, c->num_experts);
+  if (c->top_k < 1 || c->top_k > kMaxTopK)
+    return fail(MOE_ERR_SHAPE, "top_k must be in [1, %d], got %d", kMaxTopK, c->top_k);
+  if (c->max_tokens < 1 || (int64_t)c->max_tokens * c->top_k > kMaxRoutes)
+    return fail(MOE_ERR_SHAPE, "max_tokens must be >= 1 with max_tokens*top_k <= %lld, got max_tokens=%d top_k=%d",
+                (long long)kMaxRoutes, c->max_tokens, c->top_k);
+  if (c->act != MOE_ACT_BF16 && c->act != MOE_ACT_MXFP8)
+    return fail(MOE_ERR_ARG, "act must be MOE_ACT_BF16 (0) or MOE_ACT_MXFP8 (1), got %d", c->act);
+  return MOE_OK;
+}
+
+moe_status hip_fail(hipError_t e, const char* what) {
+  return fail(MOE_ERR_HIP, "%s failed: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace
+
+namespace moe {
+
+Layout make_layout(int H, int I, int E, int k, int Tmax, int act) {
+  Layout L{};
+  L.H = H; L.I = I; L.E = E; L.k = k; L.Tmax = Tmax; L.act = act;
+  L.Rmax = Tmax * k;
+  L.tiles_max = L.Rmax / kBM + (E < L.Rmax ? E : L.Rmax);
+  L.route_blocks = (L.Rmax + kRouteChunk - 1) / kRouteChunk;
+  L.w13 = make_mat_layout(2 * I, H);
+  L.w2 = make_mat_layout(H, I);
+  constexpr size_t A = 256;
+  size_t o = 0;
+  L.rp_w13_codes = o;  o = align_up(o + L.w13.codes_per_expert * E, A);
+  L.rp_w13_scales = o; o = align_up(o + L.w13.scales_per_expert * E, A);
+  L.rp_w2_codes = o;   o = align_up(o + L.w2.codes_per_expert * E, A);
+  L.rp_w2_scales = o;  o = align_up(o + L.w2.scales_per_expert * E, A);
+  L.rp_status = o;     o = align_up(o + 8, A);
+  L.rp_bytes = o;
+  const size_t R = (size_t)L.Rmax;
+  o = 0;
+  L.ws_counts = o;      o = align_up(o + 4 * (size_t)E, A);
+  L.ws_offsets = o;     o = align_up(o + 4 * (size_t)(E + 1), A);
+  L.ws_perm = o;        o = align_up(o + 4 * R, A);
+  L.ws_rowpos = o;      o = align_up(o + 4 * R, A);
+  L.ws_tiles = o;       o = align_up(o + 8 * (size_t)L.tiles_max, A);
+  L.ws_tile_count = o;  o = align_up(o + 4, A);
+  L.ws_blockcounts = o; o = align_up(o + 4 * (size_t)L.route_blocks * E, A);
+  if (act == MOE_ACT_MXFP8) {
+    L.ws_xq = o; o = align_up(o + (size_t)Tmax * H, A);
+    L.ws_xs = o; o = align_up(o + (size_t)Tmax * (H / 32), A);
+    L.ws_h = o;  o = align_up(o + 4 * R * I, A);
+    L.ws_hq = o; o = align_up(o + R * I, A);
+    L.ws_hs = o; o = align_up(o + R * (I / 32), A);
+  } else {
+    L.ws_xq = L.ws_xs = L.ws_hq = L.ws_hs = 0;
+    L.ws_h = o; o = align_up(o + 2 * R * I, A);
+  }
+  L.ws_y = o; o = align_up(o + 4 * R * H, A);
+  L.ws_bytes = o;
+  return L;
+}
+
+}  // namespace moe
+
+struct moe_mxfp4_plan_s {
+  moe_mxfp4_config cfg;
+  moe::Layout L;
+  const uint8_t* repacked;
+  hipEvent_t events[5];
+  int n_events;
+};
+
+namespace {
+
+moe::RouteOut route_out(const moe::Layout& L, uint8_t* ws) {
+  moe::RouteOut o;
+  o.counts = reinterpret_cast<int32_t*>(ws + L.ws_counts);
+  o.offsets = reinterpret_cast<int32_t*>(ws + L.ws_offsets);
+  o.perm = reinterpret_cast<int32_t*>(ws + L.ws_perm);
+  o.rowpos = reinterpret_cast<int32_t*>(ws + L.ws_rowpos);
+  o.tiles = reinterpret_cast<int2*>(ws + L.ws_tiles);
+  o.tile_count = reinterpret_cast<int32_t*>(ws + L.ws_tile_count);
+  o.blockcounts = reinterpret_cast<int32_t*>(ws + L.ws_blockcounts);
+  return o;
+}
+
+moe_status check_device() {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  hipDeviceProp_t prop;
+  e = hipGetDeviceProperties(&prop, dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDeviceProperties");
+  if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+    return fail(MOE_ERR_UNSUPPORTED, "device %d is %s; this library is built for gfx950 only", dev, prop.gcnArchName);
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_mxfp4_query_sizes(const moe_mxfp4_config* cfg, size_t* repacked_bytes, size_t* workspace_bytes) {
+  if (moe_status s = check_config(cfg)) return s;
+  if (!repacked_bytes || !workspace_bytes) return fail(MOE_ERR_ARG, "size output pointers must not be null");
+  const moe::Layout L = moe::make_layout(cfg->hidden, cfg->intermediate, cfg->num_experts, cfg->top_k,
+                                         cfg->max_tokens, cfg->act);
+  *repacked_bytes = L.rp_bytes;
+  *workspace_bytes = L.ws_bytes;
+  return ok();
+}
+
+moe_status moe_mxfp4_plan(const moe_mxfp4_config* cfg, const uint8_t* w13_codes, const uint8_t* w13_scales,
+                          const uint8_t* w2_codes, const uint8_t* w2_scales, void* repacked,
+                          size_t repacked_bytes, hipStream_t stream, moe_mxfp4_plan_t* out) {
+  if (moe_status s = check_config(cfg)) return s;
+  if (!out) return fail(MOE_ERR_ARG, "plan output pointer is null");
+  *out = nullptr;
+  const void* ptrs[] = {w13_codes, w13_scales, w2_codes, w2_scales, repacked};
+  const char* names[] = {"w13_codes", "w13_scales", "w2_codes", "w2_scales", "repacked"};
+  for (int i = 0; i < 5; ++i) {
+    if (!ptrs[i]) return fail(MOE_ERR_ARG, "%s is null", names[i]);
+    if (misaligned(ptrs[i])) return fail(MOE_ERR_ALIGN, "%s must be 16-byte aligned, got %p", names[i], ptrs[i]);
+  }
+  const moe::Layout L = moe::make_layout(cfg->hidden, cfg->intermediate, cfg->num_experts, cfg->top_k,
+                                         cfg->max_tokens, cfg->act);
+  if (repacked_bytes < L.rp_bytes)
+    return fail(MOE_ERR_WORKSPACE, "repacked buffer must hold %zu bytes, got %zu", L.rp_bytes, repacked_bytes);
+  if (moe_status s = check_device()) return s;
+  uint8_t* rp = static_cast<uint8_t*>(repacked);
+  hipError_t e = moe::launch_repack(L, w13_codes, w13_scales, w2_codes, w2_scales, rp, stream);
+  if (e != hipSuccess) return hip_fail(e, "repack launch");
+  unsigned long long status = 0;
+  e = hipMemcpyAsync(&status, rp + L.rp_status, 8, hipMemcpyDeviceToHost, stream);
+  if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(status)");
+  e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+  if (status != ~0ull) {
+    const int matrix = (int)(status >> 56);
+    const unsigned long long flat = status & ((1ull << 56) - 1);
+    const moe::MatLayout& m = matrix == 0 ? L.w13 : L.w2;
+    const unsigned long long groups = (unsigned long long)m.k / 32;
+    const unsigned long long g = flat % groups;
+    const unsigned long long row = (flat / groups) % (unsigned long long)m.n;
+    const unsigned long long ex = flat / groups / (unsigned long long)m.n;
+    const uint8_t* src = matrix == 0 ? w13_scales : w2_scales;
+    uint8_t byte = 0;
+    if (hipMemcpy(&byte, src + flat, 1, hipMemcpyDeviceToHost) != hipSuccess) byte = 0;
+    return fail(MOE_ERR_SCALE_BYTE,
+                "%s scale byte 0x%02X at expert %llu, row %llu, group %llu is not accepted "
+                "(0x00 and 0xFF never%s)",
+                matrix == 0 ? "w13" : "w2", (unsigned)byte, ex, row, g,
+                cfg->act == MOE_ACT_BF16 ? "; 0x01, 0xFD, 0xFE not on the bf16 path" : "");
+  }
+  moe_mxfp4_plan_s* p = new moe_mxfp4_plan_s();
+  p->cfg = *cfg;
+  p->L = L;
+  p->repacked = rp;
+  p->n_events = 0;
+  *out = p;
+  return ok();
+}
+
+static moe_status check_ws(const moe_mxfp4_plan_s* p, void* workspace, size_t workspace_bytes) {
+  if (!workspace) return fail(MOE_ERR_ARG, "workspace is null");
+  if (misaligned(workspace)) return fail(MOE_ERR_ALIGN, "workspace must be 16-byte aligned, got %p", workspace);
+  if (workspace_bytes < p->L.ws_bytes)
+    return fail(MOE_ERR_WORKSPACE, "workspace must hold %zu bytes, got %zu", p->L.ws_bytes, workspace_bytes);
+  return MOE_OK;
+}
+
+moe_status moe_mxfp4_forward(moe_mxfp4_plan_t p, const uint16_t* hidden, const int32_t* topk_ids,
+                             const float* topk_weights, int32_t T, float* acc_fp32, uint16_t* out_bf16,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!p) return fail(MOE_ERR_ARG, "plan is null");
+  if (T < 0) return fail(MOE_ERR_ARG, "num_tokens must be >= 0, got %d", T);
+  if (T > p->cfg.max_tokens)
+    return fail(MOE_ERR_CAPACITY, "num_tokens %d exceeds the plan's max_tokens %d", T, p->cfg.max_tokens);
+  if (moe_status s = check_ws(p, workspace, workspace_bytes)) return s;
+  const void* ptrs[] = {hidden, topk_ids, topk_weights, out_bf16};
+  const char* names[] = {"hidden", "topk_ids", "topk_weights", "out_bf16"};
+  for (int i = 0; i < 4; ++i) {
+    if (!ptrs[i]) return fail(MOE_ERR_ARG, "%s is null", names[i]);
+    if (misaligned(ptrs[i])) return fail(MOE_ERR_ALIGN, "%s must be 16-byte aligned, got %p", names[i], ptrs[i]);
+  }
+  if (acc_fp32 && misaligned(acc_fp32))
+    return fail(MOE_ERR_ALIGN, "acc_fp32 must be 16-byte aligned, got %p", (void*)acc_fp32);
+  if (T == 0) return ok();
+
+  const moe::Layout& L = p->L;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  const moe::RouteOut ro = route_out(L, ws);
+  const bool mx = p->cfg.act == MOE_ACT_MXFP8;
+  const int nev = p->n_events;
+  hipError_t e;
+#define REC(i) \
+  if (nev > (i) && (e = hipEventRecord(p->events[i], stream)) != hipSuccess) return hip_fail(e, "hipEventRecord")
+#define CHK(call, what) \
+  if ((e = (call)) != hipSuccess) return hip_fail(e, what)
+
+  REC(0);
+  CHK(moe::launch_route(L, topk_ids, T, ro, stream), "route launch");
+  if (mx) CHK(moe::launch_quant_bf16(hidden, T, L.H, ws + L.ws_xq, ws + L.ws_xs, stream), "x quant launch");
+  REC(1);
+
+  moe::FcArgs f1{};
+  f1.codes = p->repacked + L.rp_w13_codes;
+  f1.scales = p->repacked + L.rp_w13_scales;
+  f1.mat = L.w13;
+  f1.tiles = ro.tiles;
+  f1.tile_count = ro.tile_count;
+  f1.offsets = ro.offsets;
+  f1.perm = ro.perm;
+  f1.top_k = L.k;
+  f1.a = mx ? static_cast<const void*>(ws + L.ws_xq) : static_cast<const void*>(hidden);
+  f1.a_scales = mx ? ws + L.ws_xs : nullptr;
+  f1.lda = L.H;
+  f1.out = ws + L.ws_h;
+  f1.ldo = L.I;
+  const int tiles_max = (int)((int64_t)T * L.k / moe::kBM + (L.E < T * L.k ? L.E : T * L.k));
+  CHK(mx ? moe::launch_fc1_mx(f1, tiles_max, stream) : moe::launch_fc1_bf16(f1, tiles_max, stream), "FC1 launch");
+  REC(2);
+
+  if (mx)
+    CHK(moe::launch_quant_f32(reinterpret_cast<const float*>(ws + L.ws_h), ro.offsets + L.E, T * L.k, L.I,
+                              ws + L.ws_hq, ws + L.ws_hs, stream), "h quant launch");
+  moe::FcArgs f2 = f1;
+  f2.codes = p->repacked + L.rp_w2_codes;
+  f2.scales = p->repacked + L.rp_w2_scales;
+  f2.mat = L.w2;
+  f2.a = mx ? static_cast<const void*>(ws + L.ws_hq) : static_cast<const void*>(ws + L.ws_h);
+  f2.a_scales = mx ? ws + L.ws_hs : nullptr;
+  f2.lda = L.I;
+  f2.out = ws + L.ws_y;
+  f2.ldo = L.H;
+  CHK(mx ? moe::launch_fc2_mx(f2, tiles_max, stream) : moe::launch_fc2_bf16(f2, tiles_max, stream), "FC2 launch");
+  REC(3);
+
+  CHK(moe::launch_combine(reinterpret_cast<const float*>(ws + L.ws_y), ro.rowpos, topk_ids, topk_weights, T, L.k,
+                          L.H, L.E, acc_fp32, out_bf16, stream), "combine launch");
+  REC(4);
+#undef REC
+#undef CHK
+  return ok();
+}
+
+moe_status moe_mxfp4_route(moe_mxfp4_plan_t p, const int32_t* topk_ids, int32_t T, int32_t* counts,
+                           int32_t* offsets, int32_t* perm, int32_t* rowpos, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream) {
+  if (!p) return fail(MOE_ERR_ARG, "plan is null");
+  if (T < 0) return fail(MOE_ERR_ARG, "num_tokens must be >= 0, got %d", T);
+  if (T > p->cfg.max_tokens)
+    return fail(MOE_ERR_CAPACITY, "num_tokens %d exceeds the plan's max_tokens %d", T, p->cfg.max_tokens);
+  if (moe_status s = check_ws(p, workspace, workspace_bytes)) return s;
+  const void* ptrs[] = {topk_ids, counts, offsets, perm, rowpos};
+  const char* names[] = {"topk_ids", "counts", "offsets", "perm", "rowpos"};
+  for (int i = 0; i < 5; ++i) {
+    if (!ptrs[i]) return fail(MOE_ERR_ARG, "%s is null", names[i]);
+    if (misaligned(ptrs[i])) return fail(MOE_ERR_ALIGN, "%s must be 16-byte aligned, got %p", names[i], ptrs[i]);
+  }
+  moe::RouteOut o = route_out(p->L, static_cast<uint8_t*>(workspace));
+  o.counts = counts;
+  o.offsets = offsets;
+  o.perm = perm;
+  o.rowpos = rowpos;
+  hipError_t e = moe::launch_route(p->L, topk_ids, T, o, stream);
+  if (e != hipSuccess) return hip_fail(e, "route launch");
+  return ok();
+}
+
+moe_status moe_mxfp8_quantize(const uint16_t* x, int32_t rows, int32_t cols, uint8_t* codes, uint8_t* scales,
+                              hipStream_t stream) {
+  if (rows < 0) return fail(MOE_ERR_ARG, "rows must be >= 0, got %d", rows);
+  if (cols <= 0 || cols % 32) return fail(MOE_ERR_SHAPE, "cols must be a positive multiple of 32, got %d", cols);
+  if (rows == 0) return ok();
+  const void* ptrs[] = {x, codes, scales};
+  const char* names[] = {"x", "codes", "scales"};
+  for (int i = 0; i < 3; ++i) {
+    if (!ptrs[i]) return fail(MOE_ERR_ARG, "%s is null", names[i]);
+    if (misaligned(ptrs[i])) return fail(MOE_ERR_ALIGN, "%s must be 16-byte aligned, got %p", names[i], ptrs[i]);
+  }
+  hipError_t e = moe::launch_quant_bf16(x, rows, cols, codes, scales, stream);
+  if (e != hipSuccess) return hip_fail(e, "quant launch");
+  return ok();
+}
+
+moe_status moe_mxfp4_set_stage_events(moe_mxfp4_plan_t p, hipEvent_t* events, int32_t n) {
+  if (!p) return fail(MOE_ERR_ARG, "plan is null");
+  if (n != 0 && n != 5) return fail(MOE_ERR_ARG, "stage events: n must be 0 or 5, got %d", n);
+  if (n && !events) return fail(MOE_ERR_ARG, "stage events array is null");
+  for (int i = 0; i < n; ++i) p->events[i] = events[i];
+  p->n_events = n;
+  return ok();
+}
+
+void moe_mxfp4_destroy(moe_mxfp4_plan_t p) { delete p; }
+
+const char* moe_mxfp4_last_error(void) { return g_err.c_str(); }
+
+}  // extern "C"

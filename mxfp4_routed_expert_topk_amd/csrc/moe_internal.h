@@ -1,0 +1,148 @@
+// Internal declarations of the MXFP4 routed-expert MoE library (gfx950).
+//
+// Repacked weight layout (one layout serves the bf16 MFMA and the scaled
+// F8F6F4 MFMA paths).  A matrix with N rows and K columns (K-major codes
+// [N][K/2] in the checkpoint) is cut into tiles of 16 rows x 128 K:
+//   NB = N/16 row blocks, KB = K/128 column blocks.
+//   codes:  tile (nb, kb) holds 1024 bytes at ((e*NB + nb)*KB + kb)*1024;
+//           lane l (0..63) of a wave owns bytes [16l, 16l+16): row 16*nb + l%16,
+//           checkpoint bytes [64*kb + 16*(l/16), +16), i.e. the 32 consecutive K
+//           values 128*kb + 32*(l/16) + [0, 32), nibbles copied unchanged.
+//   scales: KB4 = ceil(KB/4) groups of four column blocks; group (nb, c) holds
+//           256 bytes at ((e*NB + nb)*KB4 + c)*256; byte 4l + j is the E8M0 scale
+//           of row 16*nb + l%16 for K group 4*(4c + j) + l/16 (its 32 K values are
+//           exactly lane l's in column block 4c + j); padding bytes are 127.
+// FC1 (W13, N = 2I) interleaves gate and up row blocks: row block 2j holds
+// gate rows [16j, 16j+16) and row block 2j+1 holds up rows [I+16j, I+16j+16),
+// so one workgroup owning a block pair has the gate and up columns of the
+// same 16 intermediate outputs.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kWave = 64;
+constexpr int kTileN = 16;          // rows per repacked tile
+constexpr int kTileK = 128;         // K per repacked tile
+constexpr int kTileBytes = 1024;    // codes per tile
+constexpr int kScaleGroupBytes = 256;
+constexpr int kRouteChunk = 1024;   // routes per route workgroup
+constexpr int kBM = 16;             // rows per FC tile (one MFMA M block)
+
+struct MatLayout {
+  int32_t n, k;        // logical rows / columns
+  int32_t nb, kb, kb4; // row blocks, column blocks, scale groups per row block
+  size_t codes_per_expert;   // bytes
+  size_t scales_per_expert;  // bytes
+};
+
+inline MatLayout make_mat_layout(int n, int k) {
+  MatLayout m;
+  m.n = n; m.k = k;
+  m.nb = n / kTileN; m.kb = k / kTileK; m.kb4 = (m.kb + 3) / 4;
+  m.codes_per_expert = (size_t)m.nb * m.kb * kTileBytes;
+  m.scales_per_expert = (size_t)m.nb * m.kb4 * kScaleGroupBytes;
+  return m;
+}
+
+// Offsets of every region inside the repacked buffer and the workspace.
+struct Layout {
+  int32_t H, I, E, k, Tmax, act;
+  int32_t Rmax;          // Tmax * k
+  int32_t tiles_max;     // upper bound of FC tiles (16 rows each)
+  int32_t route_blocks;  // ceil(Rmax / kRouteChunk)
+  MatLayout w13, w2;
+  // repacked buffer
+  size_t rp_w13_codes, rp_w13_scales, rp_w2_codes, rp_w2_scales, rp_status, rp_bytes;
+  // workspace
+  size_t ws_counts, ws_offsets, ws_perm, ws_rowpos, ws_tiles, ws_tile_count, ws_blockcounts;
+  size_t ws_xq, ws_xs, ws_h, ws_hq, ws_hs, ws_y, ws_bytes;
+};
+
+Layout make_layout(int H, int I, int E, int k, int Tmax, int act);
+
+// ---------------------------------------------------------------- launchers
+// All launchers enqueue on `stream` and return the launch status.
+hipError_t launch_repack(const Layout& L, const uint8_t* w13c, const uint8_t* w13s,
+                         const uint8_t* w2c, const uint8_t* w2s, uint8_t* repacked,
+                         hipStream_t stream);
+
+struct RouteOut {
+  int32_t* counts;      // [E]
+  int32_t* offsets;     // [E+1]
+  int32_t* perm;        // [Rmax]
+  int32_t* rowpos;      // [Rmax]
+  int2* tiles;          // [tiles_max] (expert, first row) of each 16-row FC tile
+  int32_t* tile_count;  // [1]
+  int32_t* blockcounts; // [route_blocks * E] scratch
+};
+hipError_t launch_route(const Layout& L, const int32_t* ids, int32_t T, const RouteOut& o,
+                        hipStream_t stream);
+
+hipError_t launch_quant_bf16(const uint16_t* x, int32_t rows, int32_t cols, uint8_t* codes,
+                             uint8_t* scales, hipStream_t stream);
+hipError_t launch_quant_f32(const float* x, const int32_t* rows_dev, int32_t rows_max,
+                            int32_t cols, uint8_t* codes, uint8_t* scales, hipStream_t stream);
+
+struct FcArgs {
+  const uint8_t* codes;     // repacked codes of the matrix (all experts)
+  const uint8_t* scales;    // repacked scales of the matrix
+  MatLayout mat;
+  const int2* tiles;
+  const int32_t* tile_count;
+  const int32_t* offsets;   // [E+1]
+  const int32_t* perm;      // FC1: gather rows of x through perm/k
+  int32_t top_k;
+  const void* a;            // FC1: x bf16 [T,H] (or E4M3 codes); FC2: h [R,I] bf16 (or E4M3 codes)
+  const uint8_t* a_scales;  // MXFP8: E8M0 per 32 of the A rows
+  int32_t lda;              // elements per A row
+  void* out;                // FC1: h ([R,I] bf16, or fp32 for MXFP8); FC2: y [R,H] fp32
+  int32_t ldo;              // elements per output row
+};
+hipError_t launch_fc1_bf16(const FcArgs& a, int tiles_max, hipStream_t stream);
+hipError_t launch_fc2_bf16(const FcArgs& a, int tiles_max, hipStream_t stream);
+hipError_t launch_fc1_mx(const FcArgs& a, int tiles_max, hipStream_t stream);
+hipError_t launch_fc2_mx(const FcArgs& a, int tiles_max, hipStream_t stream);
+
+hipError_t launch_combine(const float* y, const int32_t* rowpos, const int32_t* ids,
+                          const float* w, int32_t T, int32_t k, int32_t H, int32_t E,
+                          float* acc, uint16_t* out, hipStream_t stream);
+
+// ---------------------------------------------------------------- device helpers
+#if defined(__HIPCC__)
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+
+// E8M0 byte -> fp32 power of two (exact for bytes 1..254).
+__device__ __forceinline__ float e8m0_to_f32(uint32_t b) { return __uint_as_float(b << 23); }
+
+// Eight E2M1 codes (one dword, element 2j in the low nibble of byte j) -> eight
+// bf16 values times the power-of-two scale, on the gfx950 scaled converter
+// (it takes the exponent of `scale` only).
+__device__ __forceinline__ bf16x8_t dequant8(uint32_t w, float scale) {
+  bf16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0);
+  bf16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1);
+  bf16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2);
+  bf16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3);
+  bf16x8_t r;
+  r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
+  r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
+  return r;
+}
+
+// fp32 -> bf16 bits, round to nearest even (NaN kept quiet).
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + __expf(-z)); }
+#endif
+
+}  // namespace moe

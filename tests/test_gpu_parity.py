@@ -1,0 +1,383 @@
+"""GPU parity of the HIP path against the fp64 oracle, through the C ABI.
+
+Routing and repack: bit-exact.  Layer outputs: every row within 3 bf16 ULP
+or 4e-3 relative L2 of the oracle (oracle.check_rows), and out_bf16 equal
+bit for bit to RNE_bf16(acc_fp32).  Small shapes are compared in full; the
+full-size configurations on sampled tokens the oracle evaluates one by one.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+import mxfp4_routed_expert_topk_amd as moe
+from tests import gpu_helpers as G
+
+pytestmark = pytest.mark.gpu
+
+
+def say(msg):
+    print(f"[gpu-test] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    moe.load_library()
+
+
+def check_layer(case, out, acc, tokens=None, ew=None):
+    """Compare the device outputs of `tokens` with the oracle."""
+    sel = list(range(case.shape.tokens)) if tokens is None else list(tokens)
+    ref = oracle.forward(case.hidden_bits, case.topk_ids, case.topk_weights,
+                         ew if ew is not None else case.expert, case.shape.experts, act=case.act, tokens=sel)
+    out_bits = G.bf16_bits(out)[sel]
+    out_v = oracle.bf16_bits_to_f64(out_bits)
+    r_out = oracle.check_rows(out_v, ref)
+    assert r_out["pass"], f"{case.name} out: {r_out}"
+    if acc is not None:
+        acc_np = acc.cpu().numpy()[sel]
+        r_acc = oracle.check_rows(acc_np, ref)
+        assert r_acc["pass"], f"{case.name} acc: {r_acc}"
+        np.testing.assert_array_equal(out_bits, oracle.f32_to_bf16_rne(acc_np))
+    return r_out
+
+
+# ------------------------------------------------------------------ routing
+def small_route_plan(E, k, max_tokens):
+    case = W.make_case("route", W.LayerShape(1, 128, 128, E, E, k), 5)
+    return G.make_plan(case, max_tokens=max_tokens)[0]
+
+
+ROUTE_CASES = [(0, None), (1, 1), (1, 4), (1, 16), (1, 64), (1, 128), (2, None), (3, None), (4, None)]
+
+
+@pytest.mark.parametrize("cid,m", ROUTE_CASES)
+def test_route_bitexact(cid, m):
+    case = W.config_case(cid, m=m)
+    s = case.shape
+    say(f"route config {cid} m={m} T={s.tokens} E={s.experts}")
+    plan = small_route_plan(s.experts, s.top_k, s.tokens)
+    counts, offsets, perm, rowpos = plan.route(G.to_dev(case.topk_ids))
+    torch.cuda.synchronize()
+    want = oracle.route_sort(case.topk_ids, s.experts)
+    R = int(want[1][-1])
+    np.testing.assert_array_equal(counts.cpu().numpy(), want[0])
+    np.testing.assert_array_equal(offsets.cpu().numpy(), want[1])
+    np.testing.assert_array_equal(perm.cpu().numpy()[:R], want[2])
+    np.testing.assert_array_equal(rowpos.cpu().numpy(), want[3])
+
+
+@pytest.mark.parametrize("ids,E", [
+    (np.full((5, 3), -1, np.int32), 4),                               # all invalid
+    (np.array([[1, 1, 1], [1, 0, 1]], np.int32), 2),                   # duplicates
+    (np.array([[7, 3, 2, 9]], np.int32), 8),                           # one token, one non-resident
+    (np.random.default_rng(3).integers(-2, 40, (700, 3)).astype(np.int32), 33),   # 2100 routes: chunked path
+])
+def test_route_edge_cases(ids, E):
+    say(f"route edge case T={ids.shape[0]} k={ids.shape[1]} E={E}")
+    plan = small_route_plan(E, ids.shape[1], ids.shape[0])
+    got = plan.route(G.to_dev(ids))
+    torch.cuda.synchronize()
+    want = oracle.route_sort(ids, E)
+    R = int(want[1][-1])
+    for g, w, n in zip(got, want, (E, E + 1, R, ids.size)):
+        np.testing.assert_array_equal(g.cpu().numpy()[:n], w)
+
+
+# ------------------------------------------------------------------ repack
+@pytest.mark.parametrize("shape,act", [
+    (W.LayerShape(1, 256, 128, 8, 8, 2), "bf16"),
+    (W.LayerShape(1, 384, 640, 3, 3, 2), "mxfp8"),
+    (W.LayerShape(1, 7168, 2048, 2, 2, 8), "bf16"),
+])
+def test_repack_inverse_is_exact(shape, act):
+    case = W.make_case("rp", shape, 9, act=act)
+    say(f"repack H={shape.hidden} I={shape.inter} E={shape.experts}")
+    plan, w = G.make_plan(case)
+    torch.cuda.synchronize()
+    rp = plan.repacked.cpu().numpy()
+    E, H, I = shape.experts, shape.hidden, shape.inter
+    L13c = E * (2 * I // 16) * (H // 128) * 1024
+    L13s = E * (2 * I // 16) * ((H // 128 + 3) // 4) * 256
+    L2c = E * (H // 16) * (I // 128) * 1024
+    al = lambda n: (n + 255) // 256 * 256
+    o13s = al(L13c)
+    o2c = o13s + al(L13s)
+    o2s = o2c + al(L2c)
+    w13c, w13s, w2c, w2s = (t.cpu().numpy() for t in w)
+    np.testing.assert_array_equal(G.unrepack_codes(rp[:L13c], E, 2 * I, H, interleave_half=I), w13c)
+    s13, pad13 = G.unrepack_scales(rp[o13s:], E, 2 * I, H, interleave_half=I)
+    np.testing.assert_array_equal(s13, w13s)
+    np.testing.assert_array_equal(G.unrepack_codes(rp[o2c:], E, H, I), w2c)
+    s2, pad2 = G.unrepack_scales(rp[o2s:], E, H, I)
+    np.testing.assert_array_equal(s2, w2s)
+    assert pad13 and pad2
+
+
+# ------------------------------------------------------------------ forward, small shapes in full
+SMALL = [
+    ("tiny", lambda: W.config_case(0)),
+    ("ragged", lambda: W.make_case("ragged", W.LayerShape(37, 384, 256, 10, 12, 3), 31, routing="uniform",
+                                   invalid_frac=0.05)),
+    ("multi_tile", lambda: W.make_case("multi_tile", W.LayerShape(300, 512, 384, 4, 4, 2), 32,
+                                       routing="uniform", nan_accumulator=True)),
+    ("tiny_mx", lambda: W.make_case("tiny_mx", W.LayerShape(16, 256, 128, 8, 8, 2), 33, routing="softmax_topk",
+                                    act="mxfp8")),
+    ("ragged_mx", lambda: W.make_case("ragged_mx", W.LayerShape(45, 640, 384, 6, 7, 4), 34, routing="uniform",
+                                      invalid_frac=0.03, act="mxfp8")),
+]
+
+
+@pytest.mark.parametrize("name,make", SMALL, ids=[s[0] for s in SMALL])
+def test_forward_small_full(name, make):
+    case = make()
+    s = case.shape
+    say(f"forward {name} T={s.tokens} H={s.hidden} I={s.inter} E={s.experts} k={s.top_k} act={case.act}")
+    plan, _ = G.make_plan(case)
+    out, acc = G.run_forward(plan, case, nan_acc=True)
+    r = check_layer(case, out, acc, ew=case.experts())
+    say(f"  max_ulp={r['max_ulp']:.2f} max_rel_l2={r['max_rel_l2']:.2e}")
+
+
+# ------------------------------------------------------------------ full-size configurations, sampled tokens
+_plans = {}
+
+
+def big_plan(cid, case, max_tokens):
+    key = (cid, case.wseed, max_tokens)
+    if key not in _plans:
+        _plans.clear()
+        torch.cuda.empty_cache()
+        say(f"  generating and repacking {case.shape.experts} experts (config {cid})")
+        plan, w = G.make_plan(case, max_tokens=max_tokens)
+        del w
+        torch.cuda.synchronize()
+        _plans[key] = plan
+    return _plans[key]
+
+
+def sampled_tokens(case, n):
+    T = case.shape.tokens
+    ids = case.topk_ids
+    picks = [0, T - 1]
+    if n > 2:
+        # a token with an invalid route, and one routed to the hottest expert
+        bad = np.nonzero(((ids < 0) | (ids >= case.shape.experts)).any(axis=1))[0]
+        if bad.size:
+            picks.append(int(bad[len(bad) // 2]))
+        valid = ids[(ids >= 0) & (ids < case.shape.experts)]
+        if valid.size:
+            hot = np.bincount(valid).argmax()
+            picks.append(int(np.nonzero((ids == hot).any(axis=1))[0][-1]))
+    return sorted(set(picks)) if T > 1 else [0]
+
+
+@pytest.mark.parametrize("m", W.DECODE_M)
+def test_forward_decode(m):
+    case = W.config_case(1, m=m)
+    say(f"forward decode M={m}")
+    plan = big_plan(1, case, max(W.DECODE_M))
+    out, acc = G.run_forward(plan, case)
+    assert torch.isfinite(acc).all()
+    toks = sampled_tokens(case, 2)
+    r = check_layer(case, out, acc, tokens=toks)
+    say(f"  tokens {toks}: max_ulp={r['max_ulp']:.2f} max_rel_l2={r['max_rel_l2']:.2e}")
+
+
+@pytest.mark.parametrize("cid", [2, 3, 4])
+def test_forward_prefill(cid):
+    case = W.config_case(cid)
+    say(f"forward config {cid} ({case.name}) T={case.shape.tokens} E={case.shape.experts} act={case.act}")
+    plan = big_plan(cid, case, case.shape.tokens)
+    out, acc = G.run_forward(plan, case)
+    # the accumulator started as NaN for the fused-sum stress: all of it is overwritten
+    assert torch.isfinite(acc).all() and torch.isfinite(out.float()).all()
+    np.testing.assert_array_equal(G.bf16_bits(out), oracle.f32_to_bf16_rne(acc.cpu().numpy()))
+    toks = sampled_tokens(case, 3)
+    r = check_layer(case, out, acc, tokens=toks)
+    say(f"  tokens {toks}: max_ulp={r['max_ulp']:.2f} max_rel_l2={r['max_rel_l2']:.2e}")
+
+
+# ------------------------------------------------------------------ exact invariants (bitwise on the device)
+@pytest.fixture(scope="module")
+def mid():
+    case = W.make_case("mid", W.LayerShape(40, 512, 256, 6, 8, 3), 41, routing="uniform", invalid_frac=0.05)
+    plan, w = G.make_plan(case)
+    return case, plan, w
+
+
+def _fwd(plan, case, ids=None, wts=None, x=None):
+    import dataclasses
+    c = dataclasses.replace(case, topk_ids=case.topk_ids if ids is None else ids,
+                            topk_weights=case.topk_weights if wts is None else wts,
+                            hidden_bits=case.hidden_bits if x is None else x)
+    out, acc = G.run_forward(plan, c, nan_acc=True)
+    return G.bf16_bits(out), acc.cpu().numpy()
+
+
+def test_repeat_runs_identical_and_inputs_untouched(mid):
+    case, plan, _ = mid
+    say("invariants: repeat runs, immutable inputs")
+    x = G.to_dev(case.hidden_bits).view(torch.bfloat16)
+    ids = G.to_dev(case.topk_ids)
+    wts = G.to_dev(case.topk_weights)
+    snap = [t.clone() for t in (x, ids, wts)]
+    rp = plan.repacked.clone()
+    outs = []
+    for _ in range(3):
+        acc = torch.full((40, 512), float("nan"), device=x.device)
+        out = plan.forward(x, ids, wts, acc=acc)
+        torch.cuda.synchronize()
+        outs.append((G.bf16_bits(out), acc.cpu().numpy()))
+    for o, a in outs[1:]:
+        np.testing.assert_array_equal(o, outs[0][0])
+        np.testing.assert_array_equal(a, outs[0][1])
+    for a, b in zip(snap, (x, ids, wts)):
+        assert torch.equal(a, b)
+    assert torch.equal(rp, plan.repacked)
+
+
+def test_zero_weight_route_equals_invalid_route(mid):
+    case, plan, _ = mid
+    say("invariants: zero weight vs invalid id")
+    ids = case.topk_ids.copy()
+    t, s = np.argwhere((ids >= 0) & (ids < 6))[5]
+    w0 = case.topk_weights.copy(); w0[t, s] = 0.0
+    ids_inv = ids.copy(); ids_inv[t, s] = -1
+    w_nan = case.topk_weights.copy(); w_nan[t, s] = np.nan
+    a = _fwd(plan, case, ids, w0)
+    b = _fwd(plan, case, ids_inv, case.topk_weights)
+    c = _fwd(plan, case, ids_inv, w_nan)         # the weight of an invalid route is never read
+    np.testing.assert_array_equal(a[1], b[1])
+    np.testing.assert_array_equal(b[1], c[1])
+
+
+def test_weights_times_two_doubles_exactly(mid):
+    case, plan, _ = mid
+    say("invariants: route weights x2")
+    a = _fwd(plan, case)
+    b = _fwd(plan, case, wts=case.topk_weights * 2)
+    np.testing.assert_array_equal(b[1], 2 * a[1])
+
+
+def test_token_permutation_permutes_rows(mid):
+    case, plan, _ = mid
+    say("invariants: token permutation")
+    p = np.random.default_rng(2).permutation(case.shape.tokens)
+    a = _fwd(plan, case)
+    b = _fwd(plan, case, case.topk_ids[p], case.topk_weights[p], case.hidden_bits[p])
+    np.testing.assert_array_equal(b[1], a[1][p])
+
+
+def test_expert_relabelling_changes_nothing(mid):
+    case, plan, w = mid
+    say("invariants: expert relabelling")
+    E = case.shape.experts
+    p = np.random.default_rng(0).permutation(E)
+    inv = torch.from_numpy(np.argsort(p)).to(w[0].device)
+    plan2 = moe.Plan(plan.cfg, *(t[inv].contiguous() for t in w))
+    ids2 = case.topk_ids.copy()
+    m = (ids2 >= 0) & (ids2 < E)
+    ids2[m] = p[ids2[m]]
+    np.testing.assert_array_equal(_fwd(plan2, case, ids2)[1], _fwd(plan, case)[1])
+
+
+def test_w2_scale_plus_one_doubles_exactly(mid):
+    case, plan, w = mid
+    say("invariants: W2 scales + 1")
+    plan2 = moe.Plan(plan.cfg, w[0], w[1], w[2], (w[3] + 1).contiguous())
+    np.testing.assert_array_equal(_fwd(plan2, case)[1], 2 * _fwd(plan, case)[1])
+
+
+def test_graph_replay_matches_eager(mid):
+    case, plan, _ = mid
+    say("graph capture and replay")
+    x = G.to_dev(case.hidden_bits).view(torch.bfloat16)
+    ids = G.to_dev(case.topk_ids)
+    wts = G.to_dev(case.topk_weights)
+    acc = torch.zeros((40, 512), device=x.device)
+    out = torch.empty((40, 512), dtype=torch.bfloat16, device=x.device)
+    plan.forward(x, ids, wts, out=out, acc=acc)
+    torch.cuda.synchronize()
+    ref_out, ref_acc = out.clone(), acc.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            plan.forward(x, ids, wts, out=out, acc=acc)
+    torch.cuda.synchronize()
+    for i in range(3):
+        out.fill_(float("nan")); acc.fill_(float("nan"))
+        torch.cuda.synchronize()
+        _ = torch.randn(1000, device=x.device).sum()      # eager work between replays
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref_out.view(torch.int16)), i
+        assert torch.equal(acc, ref_acc), i
+
+
+# ------------------------------------------------------------------ error paths
+def test_errors_are_reported(mid):
+    case, plan, w = mid
+    say("error paths")
+    x = G.to_dev(case.hidden_bits).view(torch.bfloat16)
+    ids = G.to_dev(case.topk_ids)
+    wts = G.to_dev(case.topk_weights)
+    with pytest.raises(moe.MoeError) as ei:
+        plan.forward(x, ids, wts, num_tokens=41)
+    assert ei.value.status == 4 and "exceeds" in ei.value.message
+    with pytest.raises(moe.MoeError) as ei:
+        plan.forward(x, ids, wts, workspace=plan.workspace[: plan.workspace_bytes - 256])
+    assert ei.value.status == 6
+    xb = torch.empty(40 * 512 + 8, dtype=torch.bfloat16, device=x.device)
+    with pytest.raises(moe.MoeError) as ei:
+        plan.forward(xb[1:1 + 40 * 512].view(40, 512), ids, wts)
+    assert ei.value.status == 3
+    # T = 0 is a valid no-op
+    out = torch.full((1, 512), 7.0, dtype=torch.bfloat16, device=x.device)
+    plan.forward(x, ids, wts, out=out, num_tokens=0)
+    torch.cuda.synchronize()
+    assert (out == 7.0).all()
+
+
+@pytest.mark.parametrize("byte,act,bad", [(0xFF, "bf16", True), (0x00, "mxfp8", True), (0x01, "bf16", True),
+                                          (0xFE, "bf16", True), (0x01, "mxfp8", False), (0xFE, "mxfp8", False)])
+def test_scale_byte_validation(byte, act, bad):
+    case = W.make_case("sc", W.LayerShape(2, 256, 128, 3, 3, 2), 51, act=act)
+    say(f"scale byte 0x{byte:02X} act={act}")
+    w = list(G.upload_experts(case))
+    w[3][2, 100, 1] = byte
+    cfg = moe.Config(256, 128, 3, 2, 2, G.ACT[act])
+    if bad:
+        with pytest.raises(moe.MoeError) as ei:
+            moe.Plan(cfg, *w)
+        assert ei.value.status == 5
+        assert f"0x{byte:02X}" in ei.value.message and "expert 2, row 100, group 1" in ei.value.message
+    else:
+        moe.Plan(cfg, *w)
+
+
+# ------------------------------------------------------------------ MXFP8 activation quantiser
+def test_mxfp8_quantize_bitexact():
+    say("mxfp8 quantiser")
+    case = W.config_case(4)
+    x = case.hidden_bits[:512]
+    special = np.zeros((4, 7168), np.float32)
+    special[1, :32] = np.ldexp(1.0, -140)                  # subnormal block
+    special[2, :32] = 448.0 * np.ldexp(1.0, np.arange(-16, 16))    # block max exactly 448 * 2^15
+    special[2, 32:64] = 446.0                                     # just below 448: e = -1
+    special[3, ::7] = -3.0e38
+    sp_bits = torch.from_numpy(special).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    xs = np.concatenate([x, sp_bits])
+    codes, scales = moe.mxfp8_quantize(G.to_dev(xs).view(torch.bfloat16))
+    torch.cuda.synchronize()
+    want_c, want_s = oracle.mxfp8_quantize(oracle.bf16_bits_to_f64(xs))
+    np.testing.assert_array_equal(scales.cpu().numpy(), want_s)
+    np.testing.assert_array_equal(codes.cpu().numpy(), want_c)

@@ -1,0 +1,109 @@
+"""Host-side checks of the C-ABI library that need no GPU: it loads, exports
+every entry point include/moe_mxfp4.h declares, sizes buffers, and rejects
+bad arguments with a status and a message before touching a device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mxfp4_routed_expert_topk_amd as moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_mxfp4.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(moe.LIB_PATH):
+        pytest.fail(f"library not built at {moe.LIB_PATH}: run python -m mxfp4_routed_expert_topk_amd.build")
+    return moe.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_exports():
+    assert declared_functions() == sorted(moe.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert lib.moe_mxfp4_last_error() is not None
+
+
+def cfg(**kw):
+    base = dict(hidden=7168, intermediate=2048, num_experts=224, top_k=8, max_tokens=128, act=0)
+    base.update(kw)
+    return moe.Config(**base)
+
+
+def test_query_sizes_decode_shape(lib):
+    rp, ws = moe.query_sizes(cfg())
+    # 224 experts x (codes + scales of W13 and W2); 23,396,352 bytes per expert
+    # plus one 256-byte status word
+    assert rp == 224 * 23_396_352 + 256
+    assert ws >= 128 * 8 * 7168 * 4          # fp32 y rows
+    rp2, _ = moe.query_sizes(cfg(hidden=256, intermediate=128, num_experts=8))
+    # H=256 has 2 column blocks per row block, I=128 one: scale groups are padded
+    # to 4 blocks (256 bytes per row block)
+    per_expert = 16 * 2 * 1024 + 16 * 256 + 16 * 1 * 1024 + 16 * 256
+    assert rp2 == 8 * per_expert + 256
+
+
+@pytest.mark.parametrize("field,value,status,needle", [
+    ("hidden", 7000, 2, "hidden must be a multiple of 128"),
+    ("hidden", 0, 2, "hidden"),
+    ("intermediate", 100, 2, "intermediate"),
+    ("num_experts", 0, 2, "num_experts"),
+    ("num_experts", 5000, 2, "num_experts"),
+    ("top_k", 0, 2, "top_k"),
+    ("top_k", 64, 2, "top_k"),
+    ("max_tokens", 0, 2, "max_tokens"),
+    ("act", 3, 1, "act must be"),
+])
+def test_config_validation(lib, field, value, status, needle):
+    with pytest.raises(moe.MoeError) as ei:
+        moe.query_sizes(cfg(**{field: value}))
+    assert ei.value.status == status
+    assert needle in ei.value.message
+    assert str(value) in ei.value.message
+
+
+def _plan_call(lib, c, ptrs, nbytes):
+    h = ctypes.c_void_p()
+    return lib.moe_mxfp4_plan(ctypes.byref(c.c()), *ptrs, nbytes, None, ctypes.byref(h)), h
+
+
+def test_plan_argument_errors_before_any_device_call(lib):
+    c = cfg(hidden=256, intermediate=128, num_experts=8, top_k=2, max_tokens=16)
+    rp, _ = moe.query_sizes(c)
+    st, _ = _plan_call(lib, c, [None, 16, 16, 16, 16], rp)
+    assert st == 1 and b"w13_codes is null" in lib.moe_mxfp4_last_error()
+    st, _ = _plan_call(lib, c, [16, 16, 16, 16, 24], rp)
+    assert st == 3 and b"repacked must be 16-byte aligned" in lib.moe_mxfp4_last_error()
+    st, _ = _plan_call(lib, c, [16, 16, 16, 16, 32], rp - 1)
+    assert st == 6 and str(rp).encode() in lib.moe_mxfp4_last_error()
+
+
+def test_forward_and_route_reject_null_plan(lib):
+    assert lib.moe_mxfp4_forward(None, 16, 16, 16, 1, None, 16, 16, 1, None) == 1
+    assert b"plan is null" in lib.moe_mxfp4_last_error()
+    assert lib.moe_mxfp4_route(None, 16, 1, 16, 16, 16, 16, 16, 1, None) == 1
+    assert lib.moe_mxfp4_set_stage_events(None, None, 0) == 1
+
+
+def test_quantize_argument_errors(lib):
+    assert lib.moe_mxfp8_quantize(16, 2, 33, 16, 16, None) == 2
+    assert b"multiple of 32, got 33" in lib.moe_mxfp4_last_error()
+    assert lib.moe_mxfp8_quantize(None, 2, 64, 16, 16, None) == 1
+    assert lib.moe_mxfp8_quantize(16, 2, 64, 20, 16, None) == 3
+    assert lib.moe_mxfp8_quantize(16, 0, 64, 16, 16, None) == 0     # empty is a no-op
+
+
+def test_destroy_null_is_a_noop(lib):
+    lib.moe_mxfp4_destroy(None)

@@ -73,14 +73,19 @@ class Case:
     scale_hi: int
     act: str = "bf16"              # "bf16" or "mxfp8"
     nan_accumulator: bool = False  # caller's fp32 accumulator starts as NaN
+    weight_seed: Optional[int] = None  # defaults to seed
+
+    @property
+    def wseed(self) -> int:
+        return self.seed if self.weight_seed is None else self.weight_seed
 
     def expert(self, e: int):
         s = self.shape
-        return gen_expert(self.seed, e, s.hidden, s.inter, self.scale_lo, self.scale_hi)
+        return gen_expert(self.wseed, e, s.hidden, s.inter, self.scale_lo, self.scale_hi)
 
     def experts(self):
         s = self.shape
-        return gen_experts(self.seed, s.experts, s.hidden, s.inter, self.scale_lo, self.scale_hi)
+        return gen_experts(self.wseed, s.experts, s.hidden, s.inter, self.scale_lo, self.scale_hi)
 
 
 def _rng(*key: int) -> np.random.Generator:
@@ -167,11 +172,12 @@ def gen_experts(seed: int, experts: int, hidden: int, inter: int, scale_lo: int,
 
 def make_case(name: str, shape: LayerShape, seed: int, routing: str = "uniform",
               scale_lo: int = 120, scale_hi: int = 130, invalid_frac: float = 0.0,
-              zipf_s: float = 1.2, act: str = "bf16", nan_accumulator: bool = False) -> Case:
+              zipf_s: float = 1.2, act: str = "bf16", nan_accumulator: bool = False,
+              weight_seed: Optional[int] = None) -> Case:
     x = gen_hidden(seed, shape.tokens, shape.hidden)
     ids, w = gen_routes(seed, shape.tokens, shape.top_k, shape.experts, shape.experts_global,
                         kind=routing, zipf_s=zipf_s, invalid_frac=invalid_frac)
-    return Case(name, shape, seed, x, ids, w, scale_lo, scale_hi, act, nan_accumulator)
+    return Case(name, shape, seed, x, ids, w, scale_lo, scale_hi, act, nan_accumulator, weight_seed)
 
 
 DECODE_M = (1, 4, 16, 64, 128)
@@ -194,7 +200,9 @@ CONFIGS: Dict[int, dict] = {
 
 def config_case(cid: int, m: Optional[int] = None, seed: Optional[int] = None) -> Case:
     """The seeded instance of configuration ``cid`` (decode needs ``m``).
-    Default seed: 1000*cid + m for decode, 1000*cid otherwise."""
+    Default seed of activations and routes: 1000*cid + m for decode, 1000*cid
+    otherwise; expert weights always use 1000*cid, so every decode batch size
+    runs over the same experts."""
     c = dict(CONFIGS[cid])
     shape: LayerShape = c.pop("shape")
     name = c.pop("name")
@@ -205,7 +213,7 @@ def config_case(cid: int, m: Optional[int] = None, seed: Optional[int] = None) -
         name = f"{name}_m{m}"
     if seed is None:
         seed = 1000 * cid + (int(m) if cid == 1 else 0)
-    return make_case(name, shape, seed, **c)
+    return make_case(name, shape, seed, weight_seed=1000 * cid, **c)
 
 
 def touched_experts(topk_ids: np.ndarray, experts: int) -> List[int]:
