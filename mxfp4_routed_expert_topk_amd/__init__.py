@@ -171,6 +171,9 @@ class Plan:
             _check(lib.moe_mxfp4_set_stage_events(self._h, None, 0))
             self._events = None
             return
+        for ev in events:
+            if not ev.cuda_event:      # torch creates the HIP event on its first record
+                ev.record()
         arr = (ctypes.c_void_p * len(events))(*[ev.cuda_event for ev in events])
         self._events = (events, arr)   # keep alive while set
         _check(lib.moe_mxfp4_set_stage_events(self._h, arr, len(events)))

@@ -14,6 +14,7 @@ import torch
 
 import mxfp4_routed_expert_topk_amd as moe
 import workloads as W
+from workloads import device as D
 
 ACT = {"bf16": moe.MOE_ACT_BF16, "mxfp8": moe.MOE_ACT_MXFP8}
 
@@ -23,25 +24,11 @@ def dev():
 
 
 def to_dev(a: np.ndarray) -> torch.Tensor:
-    return torch.from_numpy(np.ascontiguousarray(a)).to(dev())
+    return D.to_dev(a, dev())
 
 
 def upload_experts(case: W.Case):
-    """Generate the expert weights expert by expert straight into device tensors."""
-    s = case.shape
-    E, H, I = s.experts, s.hidden, s.inter
-    d = dev()
-    w13c = torch.empty((E, 2 * I, H // 2), dtype=torch.uint8, device=d)
-    w13s = torch.empty((E, 2 * I, H // 32), dtype=torch.uint8, device=d)
-    w2c = torch.empty((E, H, I // 2), dtype=torch.uint8, device=d)
-    w2s = torch.empty((E, H, I // 32), dtype=torch.uint8, device=d)
-    for e in range(E):
-        a, b, c, x = case.expert(e)
-        w13c[e].copy_(torch.from_numpy(np.ascontiguousarray(a)))
-        w13s[e].copy_(torch.from_numpy(b))
-        w2c[e].copy_(torch.from_numpy(np.ascontiguousarray(c)))
-        w2s[e].copy_(torch.from_numpy(x))
-    return w13c, w13s, w2c, w2s
+    return D.upload_experts(case, dev())
 
 
 def make_plan(case: W.Case, max_tokens=None, weights=None):
