@@ -245,13 +245,25 @@ moe_status moe_mxfp4_forward(moe_mxfp4_plan_t p, const uint16_t* hidden, const i
   const bool mx = p->cfg.act == MOE_ACT_MXFP8;
   const int nev = p->n_events;
   hipError_t e;
-#define REC(i) \
-  if (nev > (i) && (e = hipEventRecord(p->events[i], stream)) != hipSuccess) return hip_fail(e, "hipEventRecord")
-#define CHK(call, what) \
-  if ((e = (call)) != hipSuccess) return hip_fail(e, what)
+#define REC(i)                                                                                        \
+  do {                                                                                                \
+    if (nev > (i) && (e = hipEventRecord(p->events[i], stream)) != hipSuccess)                        \
+      return hip_fail(e, "hipEventRecord");                                                           \
+  } while (0)
+#define CHK(call, what)                                                                               \
+  do {                                                                                                \
+    if ((e = (call)) != hipSuccess) return hip_fail(e, what);                                         \
+  } while (0)
+
+  // Batches with at least 16 rows per expert on average take the MFMA-bound
+  // prefill kernels (bf16 path); smaller ones the weight-streaming kernels.
+  const int R = T * L.k;
+  const bool prefill = !mx && (int64_t)R >= 16LL * L.E;
+  const int bm = prefill ? moe::prefill_rows(T, L.k, L.E) : moe::kBM;
+  const int tiles_max = R / bm + (L.E < R ? L.E : R);
 
   REC(0);
-  CHK(moe::launch_route(L, topk_ids, T, ro, stream), "route launch");
+  CHK(moe::launch_route(L, topk_ids, T, ro, bm, stream), "route launch");
   if (mx) CHK(moe::launch_quant_bf16(hidden, T, L.H, ws + L.ws_xq, ws + L.ws_xs, stream), "x quant launch");
   REC(1);
 
@@ -269,8 +281,9 @@ moe_status moe_mxfp4_forward(moe_mxfp4_plan_t p, const uint16_t* hidden, const i
   f1.lda = L.H;
   f1.out = ws + L.ws_h;
   f1.ldo = L.I;
-  const int tiles_max = (int)((int64_t)T * L.k / moe::kBM + (L.E < T * L.k ? L.E : T * L.k));
-  CHK(mx ? moe::launch_fc1_mx(f1, tiles_max, stream) : moe::launch_fc1_bf16(f1, tiles_max, stream), "FC1 launch");
+  if (prefill) CHK(moe::launch_fc1_prefill(f1, bm, tiles_max, stream), "FC1 launch");
+  else CHK(mx ? moe::launch_fc1_mx(f1, tiles_max, T, stream) : moe::launch_fc1_bf16(f1, tiles_max, T, stream),
+           "FC1 launch");
   REC(2);
 
   if (mx)
@@ -285,7 +298,9 @@ moe_status moe_mxfp4_forward(moe_mxfp4_plan_t p, const uint16_t* hidden, const i
   f2.lda = L.I;
   f2.out = ws + L.ws_y;
   f2.ldo = L.H;
-  CHK(mx ? moe::launch_fc2_mx(f2, tiles_max, stream) : moe::launch_fc2_bf16(f2, tiles_max, stream), "FC2 launch");
+  if (prefill) CHK(moe::launch_fc2_prefill(f2, bm, tiles_max, stream), "FC2 launch");
+  else CHK(mx ? moe::launch_fc2_mx(f2, tiles_max, T, stream) : moe::launch_fc2_bf16(f2, tiles_max, T, stream),
+           "FC2 launch");
   REC(3);
 
   CHK(moe::launch_combine(reinterpret_cast<const float*>(ws + L.ws_y), ro.rowpos, topk_ids, topk_weights, T, L.k,
@@ -315,7 +330,7 @@ moe_status moe_mxfp4_route(moe_mxfp4_plan_t p, const int32_t* topk_ids, int32_t 
   o.offsets = offsets;
   o.perm = perm;
   o.rowpos = rowpos;
-  hipError_t e = moe::launch_route(p->L, topk_ids, T, o, stream);
+  hipError_t e = moe::launch_route(p->L, topk_ids, T, o, moe::kBM, stream);
   if (e != hipSuccess) return hip_fail(e, "route launch");
   return ok();
 }

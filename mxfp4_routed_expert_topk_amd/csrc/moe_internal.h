@@ -74,11 +74,11 @@ struct RouteOut {
   int32_t* offsets;     // [E+1]
   int32_t* perm;        // [Rmax]
   int32_t* rowpos;      // [Rmax]
-  int2* tiles;          // [tiles_max] (expert, first row) of each 16-row FC tile
+  int2* tiles;          // [tiles_max] (expert, first row) of each bm-row FC tile
   int32_t* tile_count;  // [1]
   int32_t* blockcounts; // [route_blocks * E] scratch
 };
-hipError_t launch_route(const Layout& L, const int32_t* ids, int32_t T, const RouteOut& o,
+hipError_t launch_route(const Layout& L, const int32_t* ids, int32_t T, const RouteOut& o, int bm,
                         hipStream_t stream);
 
 hipError_t launch_quant_bf16(const uint16_t* x, int32_t rows, int32_t cols, uint8_t* codes,
@@ -101,10 +101,16 @@ struct FcArgs {
   void* out;                // FC1: h ([R,I] bf16, or fp32 for MXFP8); FC2: y [R,H] fp32
   int32_t ldo;              // elements per output row
 };
-hipError_t launch_fc1_bf16(const FcArgs& a, int tiles_max, hipStream_t stream);
-hipError_t launch_fc2_bf16(const FcArgs& a, int tiles_max, hipStream_t stream);
-hipError_t launch_fc1_mx(const FcArgs& a, int tiles_max, hipStream_t stream);
-hipError_t launch_fc2_mx(const FcArgs& a, int tiles_max, hipStream_t stream);
+// `tokens` (the batch size) only picks a schedule; results do not depend on it.
+hipError_t launch_fc1_bf16(const FcArgs& a, int tiles_max, int tokens, hipStream_t stream);
+hipError_t launch_fc2_bf16(const FcArgs& a, int tiles_max, int tokens, hipStream_t stream);
+hipError_t launch_fc1_mx(const FcArgs& a, int tiles_max, int tokens, hipStream_t stream);
+hipError_t launch_fc2_mx(const FcArgs& a, int tiles_max, int tokens, hipStream_t stream);
+
+// Prefill (MFMA-bound) FC kernels over bm-row tiles, bm in {64, 128}; bf16 path.
+int prefill_rows(int tokens, int top_k, int experts);
+hipError_t launch_fc1_prefill(const FcArgs& a, int bm, int tiles_max, hipStream_t stream);
+hipError_t launch_fc2_prefill(const FcArgs& a, int bm, int tiles_max, hipStream_t stream);
 
 hipError_t launch_combine(const float* y, const int32_t* rowpos, const int32_t* ids,
                           const float* w, int32_t T, int32_t k, int32_t H, int32_t E,

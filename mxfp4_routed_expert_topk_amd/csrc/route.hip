@@ -1,5 +1,6 @@
 // Route metadata: per-expert counts, offsets, stable permutation, row of each
-// route, and the list of 16-row FC tiles.
+// route, and the list of bm-row FC tiles (16 for the streaming kernels, 64 or
+// 128 for the prefill kernels).
 //
 // A route is a (token, slot) pair with flat index f = t*k + s.  Ids outside
 // [0, E) get no row (exact-zero contribution; b12x PR #339, commit "FC2-only
@@ -62,18 +63,18 @@ __device__ __forceinline__ uint64_t match_expert(int e, bool valid) {
 
 // Counts per expert, offsets, tile list.  `cnt` is the per-expert total
 // (thread e holds expert e).  Writes counts/offsets/tiles/tile_count.
-__device__ void finish_counts(int e, int cnt, int E, int* tmp, const RouteOut& o, int* s_offsets) {
+__device__ void finish_counts(int e, int cnt, int E, int bm, int* tmp, const RouteOut& o, int* s_offsets) {
   const int c = e < E ? cnt : 0;
   const int incl = block_inclusive_scan(c, tmp);
   const int off = incl - c;
-  const int nt = (c + kBM - 1) / kBM;
+  const int nt = (c + bm - 1) / bm;
   const int tincl = block_inclusive_scan(nt, tmp);
   const int toff = tincl - nt;
   if (e < E) {
     o.counts[e] = c;
     o.offsets[e] = off;
     if (s_offsets) s_offsets[e] = off;
-    for (int i = 0; i < nt; ++i) o.tiles[toff + i] = make_int2(e, off + i * kBM);
+    for (int i = 0; i < nt; ++i) o.tiles[toff + i] = make_int2(e, off + i * bm);
   }
   if (e == E - 1) {
     o.offsets[E] = incl;
@@ -109,7 +110,7 @@ __device__ void scatter_chunk(const int32_t* ids, int R, int E, int base, const 
 }
 
 // One workgroup: everything for R <= 1024.
-__global__ __launch_bounds__(kThreads) void route_fused(const int32_t* ids, int R, int E, RouteOut o) {
+__global__ __launch_bounds__(kThreads) void route_fused(const int32_t* ids, int R, int E, int bm, RouteOut o) {
   __shared__ int s_cnt[1024];
   __shared__ int s_off[1024];
   __shared__ int tmp[kWaves];
@@ -122,7 +123,7 @@ __global__ __launch_bounds__(kThreads) void route_fused(const int32_t* ids, int 
     if (e >= 0 && e < E) atomicAdd(&s_cnt[e], 1);
   }
   __syncthreads();
-  finish_counts(t, s_cnt[t], E, tmp, o, s_off);
+  finish_counts(t, s_cnt[t], E, bm, tmp, o, s_off);
   __syncthreads();
   scatter_chunk(ids, R, E, 0, s_off, wcnt, o);
 }
@@ -143,13 +144,13 @@ __global__ __launch_bounds__(kThreads) void route_count(const int32_t* ids, int 
 }
 
 // Chunked: totals, offsets, tiles; blockcounts become each chunk's first row per expert.
-__global__ __launch_bounds__(kThreads) void route_scan(int E, int nblk, RouteOut o) {
+__global__ __launch_bounds__(kThreads) void route_scan(int E, int nblk, int bm, RouteOut o) {
   __shared__ int tmp[kWaves];
   const int e = threadIdx.x;
   int total = 0;
   if (e < E)
     for (int b = 0; b < nblk; ++b) total += o.blockcounts[(size_t)b * E + e];
-  finish_counts(e, total, E, tmp, o, nullptr);
+  finish_counts(e, total, E, bm, tmp, o, nullptr);
   __syncthreads();
   if (e < E) {
     int run = o.offsets[e];
@@ -172,17 +173,17 @@ __global__ __launch_bounds__(kThreads) void route_scatter(const int32_t* ids, in
 
 }  // namespace
 
-hipError_t launch_route(const Layout& L, const int32_t* ids, int32_t T, const RouteOut& o,
+hipError_t launch_route(const Layout& L, const int32_t* ids, int32_t T, const RouteOut& o, int bm,
                         hipStream_t stream) {
   const int R = T * L.k;
   const int E = L.E;
   if (R <= kThreads) {
-    hipLaunchKernelGGL(route_fused, dim3(1), dim3(kThreads), 0, stream, ids, R, E, o);
+    hipLaunchKernelGGL(route_fused, dim3(1), dim3(kThreads), 0, stream, ids, R, E, bm, o);
     return hipGetLastError();
   }
   const int nblk = (R + kThreads - 1) / kThreads;
   hipLaunchKernelGGL(route_count, dim3(nblk), dim3(kThreads), 0, stream, ids, R, E, o.blockcounts);
-  hipLaunchKernelGGL(route_scan, dim3(1), dim3(kThreads), 0, stream, E, nblk, o);
+  hipLaunchKernelGGL(route_scan, dim3(1), dim3(kThreads), 0, stream, E, nblk, bm, o);
   hipLaunchKernelGGL(route_scatter, dim3(nblk), dim3(kThreads), 0, stream, ids, R, E, o);
   return hipGetLastError();
 }
