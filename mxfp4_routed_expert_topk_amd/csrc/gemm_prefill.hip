@@ -1,22 +1,31 @@
 // Grouped FC1 / FC2 for large batches (prefill): MFMA-bound tiles.
 //
 // Work item = (BM-row tile of one expert's rows, 256-column slice of the
-// weight rows).  A workgroup of four waves stages, per 128-K column block,
-// the BM gathered activation rows (bf16) and the sixteen raw repacked weight
-// tiles (E2M1 codes, 16 KB) in LDS, prefetching the next block into
-// registers while the current one is multiplied.  Each wave owns a 64-row x
-// (256/WN)-column sub-tile on v_mfma_f32_32x32x16_bf16; weights are
-// dequantised in registers from the staged codes by the gfx950 scaled
-// converter (value * 2^(scale-127), exact in bf16), so a code byte crosses
-// LDS once per wave instead of as two bf16 bytes per weight.
+// weight rows).  A workgroup of four waves runs a three-stage LDS pipeline
+// over 64-K stages: each stage holds the BM gathered activation rows (bf16),
+// the sixteen half-tiles of raw repacked E2M1 codes of the slice and their
+// E8M0 bytes, written straight from global memory by global_load_lds_dwordx4
+// (no staging registers).  Each wave owns all BM rows x one 64-column quarter
+// on v_mfma_f32_32x32x16_bf16 and dequantises its weight fragments in
+// registers with the gfx950 scaled converter (value * 2^(scale-127), exact in
+// bf16): every converted fragment feeds BM/32 MFMAs, and a code byte crosses
+// LDS once instead of as two bf16 bytes per weight.  32-row blocks that lie
+// wholly past the tile's rows (Zipf-routed experts leave many) issue no MFMA.
 //
-// MFMA K order: for step s (16 K) of a 128-K block, lane l (column n = l%32,
-// half h = l/32) multiplies K = 64h + 32(s/4) + 8(s%4) + [0, 8).  For the
-// weights these eight codes are dword s%4 of the repacked 16-byte chunk
-// lane' = n%16 + 32h + 16(s/4) of row block n/16 (one ds_read_b128 serves
-// four steps); the activation lane reads the same eight K values of its row.
-// The row's sum over K is therefore taken in a fixed order independent of
-// the tile shape and the batch.
+// MFMA K order: in the stage covering K [64q, 64q+64) of a 128-K column block
+// (q = 0, 1), step s (16 K) of lane l (column n = l%32, half h = l/32)
+// multiplies K = 64q + 32h + 8s + [0, 8): for the weights that is dword s of
+// the repacked 16-byte chunk lane' = n%16 + 16h + 32q of row block n/16; the
+// activation lane reads the same eight K values of its row.  A row's sum over
+// K is therefore taken in one fixed order whatever the tile height.
+//
+// Activations sit in LDS as 128-byte rows (one coalesced 1 KB global_load_lds
+// per eight rows) whose eight 16-byte K chunks are permuted per row by
+// swz(c, r) = c ^ (r & 7) ^ ((r >> 3) & 1).  gfx950 LDS serves a ds_read_b128
+// quarter-wave (16 lanes) from 64 four-byte banks: the sixteen rows a
+// quarter-wave reads then hit sixteen distinct 16-byte bank groups (measured:
+// the plain (r & 7) swizzle leaves rows r and r + 8 colliding, about 1.6x
+// slower; unswizzled rows about 6x slower).
 //
 // Work order: the flat list (tile, column slice) is cut into eight contiguous
 // chunks, one per XCD (workgroups are dispatched round-robin over the XCDs),
@@ -28,126 +37,204 @@ namespace {
 
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glob_void_t;
 
-constexpr int kBN = 256;             // weight rows (output columns) per workgroup
-constexpr int kBlocks = kBN / kTileN;  // 16 repacked row blocks
-constexpr int kArow = 128 * 2 + 16;  // LDS bytes per staged activation row (padded against bank conflicts)
+constexpr int kBN = 256;                 // weight rows (output columns) per workgroup
+constexpr int kBlocks = kBN / kTileN;    // 16 repacked row blocks
+constexpr int kStageK = 64;              // K per pipeline stage (half a repacked tile)
+constexpr int kHalfTile = kTileBytes / 2;
 
-// Global loads of one 128-K column block into the staging registers.
-template <int AI>
-__device__ __forceinline__ void stage_load(u32x4_t (&ra)[AI], u32x4_t (&rb)[4], uint32_t (&rs)[4],
-                                           const uint8_t* abase, const uint32_t (&aoff)[AI], const uint8_t* bptr,
-                                           size_t bstride, const uint8_t* sptr, size_t sstride, int wave, int kb) {
+template <int BM>
+struct Stage {
+  static constexpr int kA = BM * kStageK * 2;        // activation rows
+  static constexpr int kB = kBlocks * kHalfTile;     // code half-tiles
+  static constexpr int kS = kBlocks * 32 * 4;        // scale dwords of the half
+  static constexpr int kBytes = kA + kB + kS;
+};
+
+// LDS position of K chunk c (0..7) in staged activation row r.
+__device__ __forceinline__ int swz(int c, int r) { return c ^ (r & 7) ^ ((r >> 3) & 1); }
+
+// s_waitcnt with vmcnt <= n and the other counters unconstrained (gfx9 encoding).
+#define MOE_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (15 << 8) | ((((n) >> 4) & 3) << 14))
+
+// Per-lane global source pointers of one stage's global_load_lds: BM/32
+// activation chunks, two code chunks, two scale dwords.  Advance by stage:
+// activations +128 B, codes +512 B, scales per 128-K block (see scale_off).
+template <int BM>
+struct StageSrc {
+  const uint8_t* a[BM / 32];
+  const uint8_t* b[2];
+  const uint8_t* s[2];
+};
+
+__device__ __forceinline__ size_t scale_off(int st) {
+  return (size_t)(st >> 3) * kScaleGroupBytes + (size_t)(st & 1) * 128;   // group of 4 blocks, half of the lanes
+}
+
+template <int BM>
+__device__ __forceinline__ void issue_stage(uint8_t* buf, const StageSrc<BM>& src, int st, int wave) {
 #pragma unroll
-  for (int i = 0; i < AI; ++i) ra[i] = *reinterpret_cast<const u32x4_t*>(abase + aoff[i] + (size_t)kb * 256);
+  for (int j = 0; j < BM / 32; ++j)   // rows 8i..8i+7 of the stage, i = wave + 4j
+    __builtin_amdgcn_global_load_lds((glob_void_t*)(src.a[j] + (size_t)st * (kStageK * 2)),
+                                     (lds_void_t*)(buf + (wave + 4 * j) * 1024), 16, 0, 0);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    rb[i] = *reinterpret_cast<const u32x4_t*>(bptr + (wave + 4 * i) * bstride + (size_t)kb * kTileBytes);
-    rs[i] = *reinterpret_cast<const uint32_t*>(sptr + (wave + 4 * i) * sstride + (size_t)(kb >> 2) * kScaleGroupBytes);
+  for (int j = 0; j < 2; ++j)         // code half-tiles of row blocks 2i, 2i+1
+    __builtin_amdgcn_global_load_lds((glob_void_t*)(src.b[j] + (size_t)st * kHalfTile),
+                                     (lds_void_t*)(buf + Stage<BM>::kA + (wave + 4 * j) * 1024), 16, 0, 0);
+#pragma unroll
+  for (int j = 0; j < 2; ++j)         // their scale dwords
+    __builtin_amdgcn_global_load_lds((glob_void_t*)(src.s[j] + scale_off(st)),
+                                     (lds_void_t*)(buf + Stage<BM>::kA + Stage<BM>::kB + (wave + 4 * j) * 256), 4, 0,
+                                     0);
+}
+
+// The K loop for a tile whose rows fill LIVE 32-row blocks (blocks past them
+// are padding and issue nothing).
+template <int BM, int LIVE>
+__device__ __forceinline__ void k_loop(uint8_t* smem, const StageSrc<BM>& src, int S, int wave, int lane,
+                                       f32x16_t (&acc)[BM / 32][2]) {
+  constexpr int NJ = 2;
+  constexpr int LOADS = BM / 32 + 4;
+  const int n32 = lane & 31, h = lane >> 5;
+  uint8_t* cur = smem;
+  uint8_t* nxt = smem + Stage<BM>::kBytes;
+  uint8_t* nxt2 = smem + 2 * Stage<BM>::kBytes;
+  issue_stage<BM>(cur, src, 0, wave);
+  if (S > 1) issue_stage<BM>(nxt, src, 1, wave);
+  // this lane's reads inside a stage
+  const int lp = (n32 & 15) + 16 * h;
+  const int boff = (wave * (2 * NJ) + (n32 >> 4)) * kHalfTile + lp * 16;  // + 2*nj*kHalfTile
+  const int soff = Stage<BM>::kA + Stage<BM>::kB + ((wave * (2 * NJ) + (n32 >> 4)) * 32 + lp) * 4;
+  const int aoff = n32 * (kStageK * 2);
+  for (int st = 0; st < S; ++st) {
+    if (st + 1 < S) MOE_WAIT_VMCNT(LOADS);   // this wave's loads of stage st have landed
+    else MOE_WAIT_VMCNT(0);
+    // ... and every wave's; stage st-1 is fully consumed.  A bare s_barrier: the
+    // fence of __syncthreads would also drain the stages still in flight.  The
+    // empty asm statements keep the compiler from moving LDS accesses across it.
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (st + 2 < S) issue_stage<BM>(nxt2, src, st + 2, wave);
+    const int sh = ((st >> 1) & 3) * 8;
+    u32x4_t bc[NJ];
+    float bs[NJ];
+#pragma unroll
+    for (int nj = 0; nj < NJ; ++nj) {
+      bc[nj] = *reinterpret_cast<const u32x4_t*>(cur + Stage<BM>::kA + boff + 2 * nj * kHalfTile);
+      bs[nj] = e8m0_to_f32((*reinterpret_cast<const uint32_t*>(cur + soff + 2 * nj * 32 * 4) >> sh) & 0xFFu);
+    }
+    // Step s+1's activation fragments are read while step s multiplies: the
+    // scheduling barriers pin each batch of LDS reads ahead of the MFMAs that
+    // follow, so a wave waits on LDS latency once per stage, not once per step.
+    const uint8_t* arow = cur + aoff;
+    bf16x8_t Ac[LIVE], An[LIVE];
+#pragma unroll
+    for (int mi = 0; mi < LIVE; ++mi)
+      Ac[mi] = *reinterpret_cast<const bf16x8_t*>(arow + mi * 32 * (kStageK * 2) + swz(4 * h, n32) * 16);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      if (s < 3) {
+#pragma unroll
+        for (int mi = 0; mi < LIVE; ++mi)
+          An[mi] = *reinterpret_cast<const bf16x8_t*>(arow + mi * 32 * (kStageK * 2) + swz(4 * h + s + 1, n32) * 16);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      bf16x8_t B[NJ];
+#pragma unroll
+      for (int nj = 0; nj < NJ; ++nj) B[nj] = dequant8(bc[nj][s], bs[nj]);
+#pragma unroll
+      for (int mi = 0; mi < LIVE; ++mi)
+#pragma unroll
+        for (int nj = 0; nj < NJ; ++nj)
+          acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Ac[mi], B[nj], acc[mi][nj], 0, 0, 0);
+      if (s < 3) {
+#pragma unroll
+        for (int mi = 0; mi < LIVE; ++mi) Ac[mi] = An[mi];
+      }
+    }
+    uint8_t* t = cur;
+    cur = nxt;
+    nxt = nxt2;
+    nxt2 = t;
   }
 }
 
-template <bool FC1, int WM>
-__global__ __launch_bounds__(256) void fc_pre(FcArgs a, int slices) {
-  constexpr int BM = 64 * WM;
-  constexpr int WN = 4 / WM;                 // waves along N
-  constexpr int NJ = kBN / WN / 32;          // 32-column MFMA blocks per wave (4 or 2)
-  __shared__ __align__(16) uint8_t sA[BM * kArow];
-  __shared__ __align__(16) uint8_t sB[kBlocks * kTileBytes];
-  __shared__ __align__(16) uint32_t sS[kBlocks * kWave];
+template <bool FC1, int BM>
+__global__ __launch_bounds__(256, 2) void fc_pre(FcArgs a, int slices) {
+  constexpr int MI = BM / 32;                // 32-row MFMA blocks per wave (all rows of the tile)
+  constexpr int NJ = 2;                      // 32-column MFMA blocks per wave (its 64-column quarter)
+  __shared__ __align__(1024) uint8_t smem[3 * Stage<BM>::kBytes];
 
   const int ntiles = *a.tile_count;
   const int total = ntiles * slices;
-  const int xcd = blockIdx.x & 7, q = blockIdx.x >> 3;
+  const int xcd = blockIdx.x & 7, qq = blockIdx.x >> 3;
   const int chunk = (total + 7) >> 3;
-  const int w = xcd * chunk + q;
-  if (q >= chunk || w >= total) return;
+  const int w = xcd * chunk + qq;
+  if (qq >= chunk || w >= total) return;
   const int tile = w / slices, slice = w - tile * slices;
   const int2 td = a.tiles[tile];
   const int e = td.x, row0 = td.y;
   const int rows = min(BM, a.offsets[e + 1] - row0);
   const MatLayout M = a.mat;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int wm = wave / WN, wn = wave % WN;
+  const int wn = wave;                       // the four waves split the 256 columns
   const int nb0 = slice * kBlocks;
+  const int live = (rows + 31) >> 5;         // 32-row blocks holding at least one row
 
-  // ---- staging assignments
-  // A: thread t copies 16-byte column c16 = t%16 of rows t/16 + 16i
-  constexpr int AI = BM / 16;
-  const int c16 = t & 15;
-  const uint8_t* abase = static_cast<const uint8_t*>(a.a) + c16 * 16;
-  uint32_t aoff[AI];   // byte offset of each staged row's 128-K block 0 (rows < 2^31 / lda bytes)
+  StageSrc<BM> src;
+  // activation chunks this lane copies: instruction i = wave + 4j writes rows
+  // 8i..8i+7 (128 bytes each); lane L fills row 8i + L/8 at position L%8 with
+  // the K chunk c that the swizzle places there.
 #pragma unroll
-  for (int i = 0; i < AI; ++i) {
-    const int r = min((t >> 4) + 16 * i, rows - 1);
-    const int ar = FC1 ? a.perm[row0 + r] / a.top_k : row0 + r;
-    aoff[i] = (uint32_t)ar * (uint32_t)a.lda * 2u;
+  for (int j = 0; j < BM / 32; ++j) {
+    const int r = 8 * (wave + 4 * j) + (lane >> 3);
+    const int rr = min(r, rows - 1);
+    const int ar = FC1 ? a.perm[row0 + rr] / a.top_k : row0 + rr;
+    src.a[j] = static_cast<const uint8_t*>(a.a) + (size_t)ar * a.lda * 2 + swz(lane & 7, r) * 16;
   }
-  // B: thread t copies chunk lane' = t%64 of row blocks t/64 + 4i; scales likewise
-  const uint8_t* bptr = a.codes + ((size_t)e * M.nb + nb0) * M.kb * kTileBytes + (size_t)lane * 16;
-  const size_t bstride = (size_t)M.kb * kTileBytes;
-  const uint8_t* sptr = a.scales + ((size_t)e * M.nb + nb0) * M.kb4 * kScaleGroupBytes + (size_t)lane * 4;
-  const size_t sstride = (size_t)M.kb4 * kScaleGroupBytes;
-
-  u32x4_t ra[AI], rb[4];
-  uint32_t rs[4];
-  f32x16_t acc[2][NJ];
+  // codes / scales this lane copies: row block 2(wave + 4j) + lane/32, chunk or dword lane%32
 #pragma unroll
-  for (int mi = 0; mi < 2; ++mi)
+  for (int j = 0; j < 2; ++j) {
+    const int blk = nb0 + 2 * (wave + 4 * j) + (lane >> 5);
+    src.b[j] = a.codes + ((size_t)e * M.nb + blk) * M.kb * kTileBytes + (lane & 31) * 16;
+    src.s[j] = a.scales + ((size_t)e * M.nb + blk) * M.kb4 * kScaleGroupBytes + (lane & 31) * 4;
+  }
+
+  f32x16_t acc[MI][NJ];
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
     for (int nj = 0; nj < NJ; ++nj)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[mi][nj][i] = 0.f;
 
-  const int n32 = lane & 31, h = lane >> 5;
-  const int KB = M.kb;
-  stage_load<AI>(ra, rb, rs, abase, aoff, bptr, bstride, sptr, sstride, wave, 0);
-  for (int kb = 0; kb < KB; ++kb) {
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < AI; ++i) *reinterpret_cast<u32x4_t*>(sA + ((t >> 4) + 16 * i) * kArow + c16 * 16) = ra[i];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      *reinterpret_cast<u32x4_t*>(sB + (wave + 4 * i) * kTileBytes + lane * 16) = rb[i];
-      sS[(wave + 4 * i) * kWave + lane] = rs[i];
+  const int S = 2 * M.kb;    // stages
+  if constexpr (MI == 4) {
+    switch (live) {
+      case 1: k_loop<BM, 1>(smem, src, S, wave, lane, acc); break;
+      case 2: k_loop<BM, 2>(smem, src, S, wave, lane, acc); break;
+      case 3: k_loop<BM, 3>(smem, src, S, wave, lane, acc); break;
+      default: k_loop<BM, 4>(smem, src, S, wave, lane, acc); break;
     }
-    __syncthreads();
-    if (kb + 1 < KB) stage_load<AI>(ra, rb, rs, abase, aoff, bptr, bstride, sptr, sstride, wave, kb + 1);
-    const int sh = (kb & 3) * 8;
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      u32x4_t bc[NJ];
-      float bs[NJ];
-#pragma unroll
-      for (int nj = 0; nj < NJ; ++nj) {
-        const int blk = wn * (2 * NJ) + 2 * nj + (n32 >> 4);
-        const int lp = (n32 & 15) + 32 * h + 16 * c;
-        bc[nj] = *reinterpret_cast<const u32x4_t*>(sB + blk * kTileBytes + lp * 16);
-        bs[nj] = e8m0_to_f32((sS[blk * kWave + lp] >> sh) & 0xFFu);
-      }
-      const uint8_t* ap = sA + (wm * 64 + n32) * kArow + (64 * h + 32 * c) * 2;
-#pragma unroll
-      for (int s4 = 0; s4 < 4; ++s4) {
-        const bf16x8_t A0 = *reinterpret_cast<const bf16x8_t*>(ap + s4 * 16);
-        const bf16x8_t A1 = *reinterpret_cast<const bf16x8_t*>(ap + 32 * kArow + s4 * 16);
-#pragma unroll
-        for (int nj = 0; nj < NJ; ++nj) {
-          const bf16x8_t B = dequant8(bc[nj][s4], bs[nj]);
-          acc[0][nj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A0, B, acc[0][nj], 0, 0, 0);
-          acc[1][nj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A1, B, acc[1][nj], 0, 0, 0);
-        }
-      }
-    }
+  } else {
+    if (live == 1) k_loop<BM, 1>(smem, src, S, wave, lane, acc);
+    else k_loop<BM, 2>(smem, src, S, wave, lane, acc);
   }
+  const int n32 = lane & 31, h = lane >> 5;
 
   // ---- epilogue.  32x32 D layout: lane holds column n32, rows 8(i/4) + 4h + (i%4).
 #pragma unroll
-  for (int mi = 0; mi < 2; ++mi) {
+  for (int mi = 0; mi < MI; ++mi) {
+    if (mi >= live) break;
 #pragma unroll
     for (int nj = 0; nj < NJ; ++nj) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int r = wm * 64 + mi * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
+        const int r = mi * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
         const float v = acc[mi][nj][i];
         if constexpr (FC1) {
           // columns 0..15 of the block pair are gate j, 16..31 up j (interleaved row blocks)
@@ -167,27 +254,33 @@ __global__ __launch_bounds__(256) void fc_pre(FcArgs a, int slices) {
   }
 }
 
-template <bool FC1, int WM>
+template <bool FC1, int BM>
 hipError_t launch_pre(const FcArgs& a, int tiles_max, hipStream_t stream) {
   const int slices = a.mat.nb / kBlocks;
   const long long items = (long long)tiles_max * slices;
   const long long grid = (items + 7) / 8 * 8;
-  hipLaunchKernelGGL((fc_pre<FC1, WM>), dim3((unsigned)grid), dim3(256), 0, stream, a, slices);
+  hipLaunchKernelGGL((fc_pre<FC1, BM>), dim3((unsigned)grid), dim3(256), 0, stream, a, slices);
   return hipGetLastError();
 }
 
 }  // namespace
 
+#ifndef MOE_PREFILL_BM
+#define MOE_PREFILL_BM 128
+#endif
+
 int prefill_rows(int tokens, int top_k, int experts) {
-  // rows per expert on average decide the tile height (results do not depend on it)
-  return (long long)tokens * top_k >= 96LL * experts ? 128 : 64;
+  // The tile height only changes the schedule (a row's K order is fixed); 128-row
+  // tiles with all-padding 32-row blocks skipped serve every batch here.
+  (void)tokens; (void)top_k; (void)experts;
+  return MOE_PREFILL_BM;
 }
 
 hipError_t launch_fc1_prefill(const FcArgs& a, int bm, int tiles_max, hipStream_t s) {
-  return bm == 128 ? launch_pre<true, 2>(a, tiles_max, s) : launch_pre<true, 1>(a, tiles_max, s);
+  return bm == 128 ? launch_pre<true, 128>(a, tiles_max, s) : launch_pre<true, 64>(a, tiles_max, s);
 }
 hipError_t launch_fc2_prefill(const FcArgs& a, int bm, int tiles_max, hipStream_t s) {
-  return bm == 128 ? launch_pre<false, 2>(a, tiles_max, s) : launch_pre<false, 1>(a, tiles_max, s);
+  return bm == 128 ? launch_pre<false, 128>(a, tiles_max, s) : launch_pre<false, 64>(a, tiles_max, s);
 }
 
 }  // namespace moe
