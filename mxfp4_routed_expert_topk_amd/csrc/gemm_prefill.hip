@@ -56,8 +56,10 @@ struct Stage {
 // LDS position of K chunk c (0..7) in staged activation row r.
 __device__ __forceinline__ int swz(int c, int r) { return c ^ (r & 7) ^ ((r >> 3) & 1); }
 
-// s_waitcnt with vmcnt <= n and the other counters unconstrained (gfx9 encoding).
-#define MOE_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (15 << 8) | ((((n) >> 4) & 3) << 14))
+// s_waitcnt with vmcnt <= n and lgkmcnt 0 (gfx9 encoding): before a stage's
+// barrier every LDS read of the previous stage has returned, whatever MFMA
+// the compiler placed after the barrier still reads its result.
+#define MOE_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | ((((n) >> 4) & 3) << 14))
 
 // Per-lane global source pointers of one stage's global_load_lds: BM/32
 // activation chunks, two code chunks, two scale dwords.  Advance by stage:

@@ -1,0 +1,256 @@
+// Grouped FC1 / FC2 for large batches on the MXFP8 path: E4M3 activations
+// with one E8M0 per 32 along K times E2M1 weights with one E8M0 per 32, on
+// the gfx950 scaled MFMA v_mfma_scale_f32_16x16x128_f8f6f4, which applies both
+// block scales inside the instruction (the OCP MX product; the MXFP8 x MXFP4
+// variant of the grouped GEMM).
+//
+// Work item = (128-row tile of one expert's rows, 256-column slice of the
+// weight rows).  The weights are what the batch streams from HBM (an expert
+// holds 23.4 MB of codes and scales at hidden 7168 / intermediate 2048, while
+// its ~85 routed rows of E4M3 activations hold 0.6 MB), so one tile covers
+// every row an expert has in a balanced batch and each weight byte is read
+// once.  A workgroup of eight waves (two per SIMD, one workgroup per CU) runs
+// one stage per 128-K column block:
+//  * weights: the repacked 1 KB tile is already the MFMA's B operand (lane l
+//    holds the 32 codes of row l%16, K group l/16), so each wave loads its two
+//    row blocks straight into registers, kDepth stages ahead, with their E8M0
+//    bytes (buffer loads: one VGPR offset, SGPR bases);
+//  * activations: the tile's rows (gathered through the route permutation
+//    for FC1) are shared by the eight waves, so they and their E8M0 bytes are
+//    copied global->LDS by buffer_load ... lds, kDepth stages ahead, into
+//    128-byte rows under the same conflict-free chunk swizzle as the bf16
+//    prefill kernel; each lane reads its A operand (bytes 16(l/16).. and
+//    64+16(l/16).. of row l%16) with two ds_read_b128 and its scale byte
+//    (K group l/16) with one ds_read_u8.
+// Each wave owns all rows x 32 columns (one gate/up pair for FC1): 2*LIVE
+// 16-row blocks by two row blocks; 32-row blocks wholly past the tile's rows
+// are neither copied nor multiplied.
+//
+// K order: a row's sum runs over the 128-K column blocks in ascending order,
+// each block one MFMA step, whatever the tile height.
+//
+// FC1: row blocks come in (gate j, up j) pairs (interleaved repack); the
+// epilogue stores h = silu(g) * u in fp32 for the MXFP8 requantisation.  FC2:
+// fp32 y rows in route-row order.
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+constexpr int kRows = kPrefillMxRows;       // rows per tile
+constexpr int kWaves = 8;
+constexpr int kNBW = 2;                     // row blocks (16 output columns each) per wave
+constexpr int kBlocks = kWaves * kNBW;      // per workgroup: 256 output columns
+constexpr int kDepth = 3;                   // stages loaded ahead of the one multiplied
+constexpr int kBufs = kDepth + 1;           // LDS stage buffers
+constexpr int kStageBytes = kRows * kTileK;   // 128 rows x 128 E4M3
+constexpr int kStageScaleBytes = kRows * 4;   // their four E8M0 bytes
+constexpr int kRsrcWord3 = 0x00020000;        // raw buffer, 32-bit data format
+
+// vmcnt <= n with lgkmcnt 0 (every LDS read of the previous stage returned)
+#define MOE_WAIT_VM_LGKM(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | ((((n) >> 4) & 3) << 14))
+
+__device__ __forceinline__ int swz(int c, int r) { return c ^ (r & 7) ^ ((r >> 3) & 1); }
+
+// Wait until at most `ahead` stage groups of this wave's loads are still
+// outstanding; a group is na + B loads (na, ahead wave-uniform; s_waitcnt takes
+// an immediate, hence the cases).
+template <int B>
+__device__ __forceinline__ void wait_groups(int ahead, int na) {
+#define MOE_W(NA)                                         \
+  if (na == NA) {                                         \
+    if (ahead >= 2) MOE_WAIT_VM_LGKM(2 * (NA + B));       \
+    else if (ahead == 1) MOE_WAIT_VM_LGKM(NA + B);        \
+    else MOE_WAIT_VM_LGKM(0);                             \
+    return;                                               \
+  }
+  MOE_W(0) MOE_W(1) MOE_W(2)
+#undef MOE_W
+  MOE_WAIT_VM_LGKM(0);
+}
+static_assert(kDepth <= 3, "wait_groups covers up to two stage groups in flight behind the current one");
+
+template <bool FC1, int LIVE>
+__device__ __forceinline__ void tile_body(const FcArgs& a, uint8_t* sa, uint8_t* ss, int e, int row0, int rows,
+                                          int slice) {
+  constexpr int MB = 2 * LIVE;            // 16-row MFMA blocks
+  constexpr int GROUPS = 4 * LIVE;        // 8-row copy groups of the live rows
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const MatLayout M = a.mat;
+  const int S = M.kb;                     // one stage per 128-K column block
+  const int sgroups = a.lda / 32;         // E8M0 bytes per activation row
+
+  // Buffer resources over the whole activation matrix and its scales: every
+  // address is a 32-bit offset from an SGPR base.
+  const __amdgpu_buffer_rsrc_t racts =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(a.a), (short)0, a.a_rows * a.lda, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rascl = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(a.a_scales), (short)0, a.a_rows * sgroups, kRsrcWord3);
+  // activation copies: group g (rows 8g .. 8g+7) is copied by wave g % 8; lane
+  // L fills row 8g + L/8 at chunk position L%8
+  const int na = (GROUPS - wave + kWaves - 1) / kWaves;   // this wave's groups: 0, 1 or 2
+  uint32_t aoff[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int r = 8 * (wave + kWaves * j) + (lane >> 3);
+    const int rr = min(r, rows - 1);
+    const int ar = FC1 ? a.perm[row0 + rr] / a.top_k : row0 + rr;
+    aoff[j] = (uint32_t)ar * (uint32_t)a.lda + swz(lane & 7, r) * 16;
+  }
+  // scale copy: lanes 0..15 each fill the dword of row 16 wave + L: its four
+  // E8M0 bytes of the stage, one per K group (rows are 4-byte aligned:
+  // sgroups is a multiple of 4)
+  uint32_t sofs;
+  {
+    const int rr = min(16 * wave + (lane & 15), rows - 1);
+    const int ar = FC1 ? a.perm[row0 + rr] / a.top_k : row0 + rr;
+    sofs = (uint32_t)ar * (uint32_t)sgroups;
+  }
+  // this wave's two weight row blocks, as buffer resources sized to them
+  const int nb0 = slice * kBlocks + wave * kNBW;
+  const uint32_t bstride = (uint32_t)M.kb * kTileBytes, sstride = (uint32_t)M.kb4 * kScaleGroupBytes;
+  const __amdgpu_buffer_rsrc_t rcode = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(a.codes) + ((size_t)e * M.nb + nb0) * bstride, (short)0, (int)(kNBW * bstride), kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rscale = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(a.scales) + ((size_t)e * M.nb + nb0) * sstride, (short)0, (int)(kNBW * sstride),
+      kRsrcWord3);
+
+  f32x4_t acc[MB][kNBW];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int j = 0; j < kNBW; ++j) acc[mb][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  u32x4_t bq[kDepth][kNBW];
+  uint32_t bs[kDepth][kNBW];
+
+  auto issue_lds = [&](int s) {
+    uint8_t* buf = sa + (s % kBufs) * kStageBytes;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      if (j < na)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(racts, (lds_void_t*)(buf + (wave + kWaves * j) * 1024), 16,
+                                                 aoff[j], s * kTileK, 0, 0);
+    if (lane < 16)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rascl, (lds_void_t*)(ss + (s % kBufs) * kStageScaleBytes + wave * 64),
+                                               4, sofs, 4 * s, 0, 0);
+  };
+  auto load_regs = [&](u32x4_t (&q)[kNBW], uint32_t (&sb)[kNBW], int s) {
+#pragma unroll
+    for (int j = 0; j < kNBW; ++j)
+      q[j] = __builtin_amdgcn_raw_buffer_load_b128(rcode, lane * 16, j * bstride + s * kTileBytes, 0);
+#pragma unroll
+    for (int j = 0; j < kNBW; ++j)
+      sb[j] = __builtin_amdgcn_raw_buffer_load_b8(rscale, lane * 4,
+                                                  j * sstride + (s >> 2) * kScaleGroupBytes + (s & 3), 0);
+  };
+
+  // A operand position of this lane inside a staged 16-row block
+  const int rl = lane & 15, q = lane >> 4;
+  const int lo_off = rl * kTileK + swz(q, rl) * 16;
+  const int hi_off = rl * kTileK + swz(4 + q, rl) * 16;
+  const int s_off = rl * 4 + q;
+
+#pragma unroll
+  for (int d = 0; d < kDepth; ++d)
+    if (d < S) {
+      issue_lds(d);
+      load_regs(bq[d], bs[d], d);
+    }
+
+  for (int s0 = 0; s0 < S; s0 += kDepth) {
+#pragma unroll
+    for (int p = 0; p < kDepth; ++p) {
+      const int st = s0 + p;
+      if (st < S) {
+        // this wave's loads of stage st have landed (those of the stages after
+        // it may still be in flight) and its LDS reads of stage st-1 have
+        // returned; the barrier extends both to every wave
+        wait_groups<1 + 2 * kNBW>(min(kDepth - 1, S - 1 - st), na);
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        if (st + kDepth < S) issue_lds(st + kDepth);   // into the buffers of stage st-1
+        const uint8_t* cur = sa + (st % kBufs) * kStageBytes;
+        const uint8_t* curs = ss + (st % kBufs) * kStageScaleBytes;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(cur + mb * 16 * kTileK + lo_off);
+          const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(cur + mb * 16 * kTileK + hi_off);
+          const int sc = curs[mb * 64 + s_off];
+          const i32x8_t Af = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                              (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+#pragma unroll
+          for (int j = 0; j < kNBW; ++j) {
+            const i32x8_t Bf = {(int)bq[p][j][0], (int)bq[p][j][1], (int)bq[p][j][2], (int)bq[p][j][3], 0, 0, 0, 0};
+            acc[mb][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(Af, Bf, acc[mb][j], 0, 4, 0, sc, 0,
+                                                                          (int)bs[p][j]);
+          }
+        }
+        if (st + kDepth < S) load_regs(bq[p], bs[p], st + kDepth);
+      }
+    }
+  }
+
+  // ---- epilogue.  16x16 D layout: lane holds column l%16, rows 4(l/16) + i.
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * mb + 4 * q + i;
+      if (r >= rows) continue;
+      float* orow = static_cast<float*>(a.out) + (size_t)(row0 + r) * a.ldo;
+      if constexpr (FC1) {
+        orow[(size_t)(nb0 / 2) * kTileN + rl] = silu_f32(acc[mb][0][i]) * acc[mb][1][i];
+      } else {
+#pragma unroll
+        for (int j = 0; j < kNBW; ++j) orow[(size_t)(nb0 + j) * kTileN + rl] = acc[mb][j][i];
+      }
+    }
+  }
+}
+
+template <bool FC1>
+__global__ __launch_bounds__(kWaves * kWave, 1) void fc_pre_mx(FcArgs a, int slices) {
+  __shared__ __align__(1024) uint8_t sa[kBufs * kStageBytes];
+  __shared__ __align__(16) uint8_t ss[kBufs * kStageScaleBytes];
+  const int ntiles = *a.tile_count;
+  const int total = ntiles * slices;
+  // eight contiguous chunks of the (tile, slice) list, one per XCD
+  const int xcd = blockIdx.x & 7, qq = blockIdx.x >> 3;
+  const int chunk = (total + 7) >> 3;
+  const int w = xcd * chunk + qq;
+  if (qq >= chunk || w >= total) return;
+  const int tile = w / slices, slice = w - tile * slices;
+  const int2 td = a.tiles[tile];
+  const int e = td.x, row0 = td.y;
+  const int rows = min(kRows, a.offsets[e + 1] - row0);
+  switch ((rows + 31) >> 5) {
+    case 1: tile_body<FC1, 1>(a, sa, ss, e, row0, rows, slice); break;
+    case 2: tile_body<FC1, 2>(a, sa, ss, e, row0, rows, slice); break;
+    case 3: tile_body<FC1, 3>(a, sa, ss, e, row0, rows, slice); break;
+    default: tile_body<FC1, 4>(a, sa, ss, e, row0, rows, slice); break;
+  }
+}
+
+template <bool FC1>
+hipError_t launch(const FcArgs& a, int tiles_max, hipStream_t stream) {
+  const int slices = a.mat.nb / kBlocks;
+  const long long items = (long long)tiles_max * slices;
+  const long long grid = (items + 7) / 8 * 8;
+  hipLaunchKernelGGL((fc_pre_mx<FC1>), dim3((unsigned)grid), dim3(kWaves * kWave), 0, stream, a, slices);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fc1_prefill_mx(const FcArgs& a, int tiles_max, hipStream_t s) { return launch<true>(a, tiles_max, s); }
+hipError_t launch_fc2_prefill_mx(const FcArgs& a, int tiles_max, hipStream_t s) {
+  return launch<false>(a, tiles_max, s);
+}
+
+}  // namespace moe

@@ -255,11 +255,15 @@ moe_status moe_mxfp4_forward(moe_mxfp4_plan_t p, const uint16_t* hidden, const i
     if ((e = (call)) != hipSuccess) return hip_fail(e, what);                                         \
   } while (0)
 
-  // Batches with at least 16 rows per expert on average take the MFMA-bound
-  // prefill kernels (bf16 path); smaller ones the weight-streaming kernels.
+  // Batches with at least 16 rows per expert on average take the 128-row-tile
+  // prefill kernels, smaller ones the 16-row weight-streaming kernels.  The
+  // prefill kernels cut N into 256-column slices (FC2's N is H; FC1's 2I always
+  // divides), and the MXFP8 one addresses its activations with 32-bit offsets.
   const int R = T * L.k;
-  const bool prefill = !mx && (int64_t)R >= 16LL * L.E;
-  const int bm = prefill ? moe::prefill_rows(T, L.k, L.E) : moe::kBM;
+  const bool large = (int64_t)R >= 16LL * L.E && L.H % 256 == 0;
+  const bool prefill = large && !mx;
+  const bool prefill_mx = large && mx && (int64_t)T * L.H < (1LL << 31) && (int64_t)R * L.I < (1LL << 31);
+  const int bm = prefill ? moe::prefill_rows(T, L.k, L.E) : prefill_mx ? moe::kPrefillMxRows : moe::kBM;
   const int tiles_max = R / bm + (L.E < R ? L.E : R);
 
   REC(0);
@@ -279,9 +283,11 @@ moe_status moe_mxfp4_forward(moe_mxfp4_plan_t p, const uint16_t* hidden, const i
   f1.a = mx ? static_cast<const void*>(ws + L.ws_xq) : static_cast<const void*>(hidden);
   f1.a_scales = mx ? ws + L.ws_xs : nullptr;
   f1.lda = L.H;
+  f1.a_rows = T;
   f1.out = ws + L.ws_h;
   f1.ldo = L.I;
   if (prefill) CHK(moe::launch_fc1_prefill(f1, bm, tiles_max, stream), "FC1 launch");
+  else if (prefill_mx) CHK(moe::launch_fc1_prefill_mx(f1, tiles_max, stream), "FC1 launch");
   else CHK(mx ? moe::launch_fc1_mx(f1, tiles_max, T, stream) : moe::launch_fc1_bf16(f1, tiles_max, T, stream),
            "FC1 launch");
   REC(2);
@@ -296,9 +302,11 @@ moe_status moe_mxfp4_forward(moe_mxfp4_plan_t p, const uint16_t* hidden, const i
   f2.a = mx ? static_cast<const void*>(ws + L.ws_hq) : static_cast<const void*>(ws + L.ws_h);
   f2.a_scales = mx ? ws + L.ws_hs : nullptr;
   f2.lda = L.I;
+  f2.a_rows = R;
   f2.out = ws + L.ws_y;
   f2.ldo = L.H;
   if (prefill) CHK(moe::launch_fc2_prefill(f2, bm, tiles_max, stream), "FC2 launch");
+  else if (prefill_mx) CHK(moe::launch_fc2_prefill_mx(f2, tiles_max, stream), "FC2 launch");
   else CHK(mx ? moe::launch_fc2_mx(f2, tiles_max, T, stream) : moe::launch_fc2_bf16(f2, tiles_max, T, stream),
            "FC2 launch");
   REC(3);

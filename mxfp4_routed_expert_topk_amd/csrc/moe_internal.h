@@ -98,6 +98,7 @@ struct FcArgs {
   const void* a;            // FC1: x bf16 [T,H] (or E4M3 codes); FC2: h [R,I] bf16 (or E4M3 codes)
   const uint8_t* a_scales;  // MXFP8: E8M0 per 32 of the A rows
   int32_t lda;              // elements per A row
+  int32_t a_rows;           // rows of A (FC1: tokens; FC2: routes)
   void* out;                // FC1: h ([R,I] bf16, or fp32 for MXFP8); FC2: y [R,H] fp32
   int32_t ldo;              // elements per output row
 };
@@ -107,10 +108,16 @@ hipError_t launch_fc2_bf16(const FcArgs& a, int tiles_max, int tokens, hipStream
 hipError_t launch_fc1_mx(const FcArgs& a, int tiles_max, int tokens, hipStream_t stream);
 hipError_t launch_fc2_mx(const FcArgs& a, int tiles_max, int tokens, hipStream_t stream);
 
-// Prefill (MFMA-bound) FC kernels over bm-row tiles, bm in {64, 128}; bf16 path.
+// Prefill (MFMA-bound) FC kernels over bm-row tiles, bm in {64, 128}; bf16 path
+// (needs N % 256 == 0).
 int prefill_rows(int tokens, int top_k, int experts);
 hipError_t launch_fc1_prefill(const FcArgs& a, int bm, int tiles_max, hipStream_t stream);
 hipError_t launch_fc2_prefill(const FcArgs& a, int bm, int tiles_max, hipStream_t stream);
+// Prefill FC kernels of the MXFP8 path over 128-row tiles (needs N % 256 == 0
+// and A plus its scales addressable with 32-bit offsets).
+constexpr int kPrefillMxRows = 128;
+hipError_t launch_fc1_prefill_mx(const FcArgs& a, int tiles_max, hipStream_t stream);
+hipError_t launch_fc2_prefill_mx(const FcArgs& a, int tiles_max, hipStream_t stream);
 
 hipError_t launch_combine(const float* y, const int32_t* rowpos, const int32_t* ids,
                           const float* w, int32_t T, int32_t k, int32_t H, int32_t E,

@@ -22,8 +22,8 @@ from .formats import (E2M1_MAGNITUDES, E4M3_MAX, bf16_bits_to_f64, dequant_mxfp4
                       e4m3_encode, e4m3_value, e8m0_value, f32_to_bf16_rne, pack_nibbles,
                       ulp_bf16, unpack_nibbles, validate_scale_bytes)
 from .route import route_sort, route_sort_by_key
-from .moe import (expert_mlp, forward, mxfp8_dequantize, mxfp8_quantize, mxfp8_roundtrip,
-                  mxfp8_scale_exponent, silu)
+from .moe import (expert_mlp, forward, fp32_dot_bound, mxfp8_dequantize, mxfp8_quantize,
+                  mxfp8_roundtrip, mxfp8_roundtrip_spread, mxfp8_scale_exponent, silu)
 from .compare import check_rows, rel_l2
 from .brute import forward_brute, e2m1_closed_form
 

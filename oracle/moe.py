@@ -18,7 +18,10 @@ Everything is fp64 with no intermediate rounding; x enters as its exact
 bfloat16 value and the weights as their exact MXFP4 values.
 
 MXFP8 variant: x (before FC1) and h (before FC2) are replaced by their MXFP8
-round trip, blocks of 32 along K (``mxfp8_quantize``).
+round trip, blocks of 32 along K (``mxfp8_quantize``).  x is exact, so its
+codes are unique; h is not: an implementation that holds h in fp32 may land
+on the other side of a rounding decision where the exact h sits within fp32
+rounding of one, and ``forward(..., with_spread=True)`` bounds the effect.
 
 The whole-layer results are reached exactly by the definition; the per-expert
 grouping below is only a way to evaluate it: each route's y is computed from
@@ -98,6 +101,59 @@ def mxfp8_roundtrip(v: np.ndarray) -> np.ndarray:
     return mxfp8_dequantize(*mxfp8_quantize(v))
 
 
+def _roundtrip_at(blocks: np.ndarray, exps: np.ndarray) -> np.ndarray:
+    """MXFP8 round trip of [n, nb, 32] values with the given block exponents."""
+    return np.ldexp(e4m3_value(e4m3_encode(np.ldexp(blocks, -exps[:, :, None]))), exps[:, :, None])
+
+
+def mxfp8_roundtrip_spread(v: np.ndarray, dv: np.ndarray):
+    """(round trip of v, spread): spread[i] bounds |rt(v')[i] - rt(v)[i]| over
+    every v' with |v' - v| <= dv elementwise.
+
+    The quantiser is a step function: a value within dv of a rounding midpoint,
+    or a block whose maximum is within its elements' dv of a scale boundary
+    448 * 2^e, has more than one correct round trip when v itself is only known
+    to within dv.  Each block exponent the block maximum can take inside its
+    interval is tried; at each, the code of v' lies between the codes of v - dv
+    and v + dv (rounding to nearest even and saturation are monotone).
+    """
+    x = np.asarray(v, dtype=np.float64)
+    d = np.broadcast_to(np.abs(np.asarray(dv, dtype=np.float64)), x.shape)
+    k = x.shape[-1]
+    if k % MXFP8_BLOCK:
+        raise ValueError("K must be a multiple of 32")
+    nb = k // MXFP8_BLOCK
+    blocks = x.reshape(-1, nb, MXFP8_BLOCK)
+    dblk = d.reshape(-1, nb, MXFP8_BLOCK)
+    mag = np.abs(blocks)
+    expo = np.vectorize(mxfp8_scale_exponent, otypes=[np.int64])
+    if blocks.size == 0:
+        return x.copy(), np.zeros_like(x)
+    e0 = expo(mag.max(axis=2))
+    e_lo = expo(np.maximum(mag - dblk, 0.0).max(axis=2))
+    e_hi = expo((mag + dblk).max(axis=2))
+    rt = _roundtrip_at(blocks, e0)
+    spread = np.zeros_like(rt)
+    for off in range(int((e_hi - e_lo).max()) + 1):
+        e = np.minimum(e_lo + off, e_hi)
+        lo = _roundtrip_at(blocks - dblk, e)
+        hi = _roundtrip_at(blocks + dblk, e)
+        spread = np.maximum(spread, np.maximum(np.abs(lo - rt), np.abs(hi - rt)))
+    return rt.reshape(x.shape), spread.reshape(x.shape)
+
+
+# fp32 rounding of the h that the MXFP8 path requantises.  A K-long dot product
+# evaluated as MFMA steps of 128 products (an adder tree of depth 7 with fp32
+# rounding) chained through an fp32 accumulator differs from the exact sum by
+# at most (7 + K/128) * 2^-24 * sum|terms|; silu and the gate product add a
+# few more roundings.  Twice that is the allowance used for h.
+FP32_EPS = 2.0 ** -24
+
+
+def fp32_dot_bound(k: int) -> float:
+    return 2.0 * (7 + -(-k // 128) + 4) * FP32_EPS
+
+
 # --------------------------------------------------------------------------- forward
 def _expert_getter(weights: ExpertSource):
     if callable(weights):
@@ -106,27 +162,50 @@ def _expert_getter(weights: ExpertSource):
     return lambda e: (w13c[e], w13s[e], w2c[e], w2s[e])
 
 
-def expert_mlp(x_rows: np.ndarray, w13c, w13s, w2c, w2s, act: str = "bf16") -> np.ndarray:
-    """y rows for one expert: W2 (silu(w1 x) * (w3 x)), fp64 throughout."""
+def expert_mlp(x_rows: np.ndarray, w13c, w13s, w2c, w2s, act: str = "bf16", with_spread: bool = False):
+    """y rows for one expert: W2 (silu(w1 x) * (w3 x)), fp64 throughout.
+
+    ``with_spread`` (MXFP8 only) also returns a per-element bound on how far y
+    can move when h carries fp32 rounding (``fp32_dot_bound``) and so may be
+    requantised on the other side of a rounding decision: |W2| times the
+    round-trip spread of h.  For bf16 the bound is zero.
+    """
     w13 = dequant_mxfp4(w13c, w13s)                  # [2I, H]
     inter = w13.shape[0] // 2
     gu = x_rows @ w13.T                               # [r, 2I]
-    h = silu(gu[:, :inter]) * gu[:, inter:]
-    if act == "mxfp8":
-        h = mxfp8_roundtrip(h)
+    g, u = gu[:, :inter], gu[:, inter:]
+    h = silu(g) * u
     w2 = dequant_mxfp4(w2c, w2s)                      # [H, I]
-    return h @ w2.T                                   # [r, H]
+    spread = None
+    if act == "mxfp8":
+        if with_spread:
+            gam = fp32_dot_bound(x_rows.shape[1])
+            absum = np.abs(x_rows) @ np.abs(w13).T    # sum of |terms| of every dot product
+            dg, du = gam * absum[:, :inter], gam * absum[:, inter:]
+            # |silu'| <= 1.1: |dh| <= 1.1 dg (|u| + du) + |silu(g)| du, plus rounding of h
+            dh = 1.1 * dg * (np.abs(u) + du) + np.abs(silu(g)) * du + 8 * FP32_EPS * np.abs(h)
+            h, sp = mxfp8_roundtrip_spread(h, dh)
+            spread = sp @ np.abs(w2).T
+        else:
+            h = mxfp8_roundtrip(h)
+    y = h @ w2.T                                      # [r, H]
+    if with_spread:
+        return y, (spread if spread is not None else np.zeros_like(y))
+    return y
 
 
 def forward(hidden_bits: np.ndarray, topk_ids: np.ndarray, topk_weights: np.ndarray,
             weights: ExpertSource, experts: int, act: str = "bf16",
-            tokens: Optional[Sequence[int]] = None) -> np.ndarray:
+            tokens: Optional[Sequence[int]] = None, with_spread: bool = False):
     """fp64 accumulator [len(tokens) or T, H] of the MoE layer.
 
     ``weights``: stacked checkpoint-layout arrays (w13_codes [E,2I,H/2],
     w13_scales [E,2I,H/32], w2_codes [E,H,I/2], w2_scales [E,H,I/32]) or a
     callable returning one expert's four arrays.  ``tokens``: evaluate only
-    these tokens (rows of the result follow this order).
+    these tokens (rows of the result follow this order).  ``with_spread``:
+    also return sum_s |w[t,s]| * (the y bound of ``expert_mlp``), the most
+    an fp32 evaluation may differ from the accumulator through rounding
+    decisions of the MXFP8 requantisation of h (zero for bf16).
     """
     if act not in ("bf16", "mxfp8"):
         raise ValueError(f"unknown activation format {act!r}")
@@ -147,16 +226,22 @@ def forward(hidden_bits: np.ndarray, topk_ids: np.ndarray, topk_weights: np.ndar
             e = int(ids[t, s])
             if 0 <= e < experts:
                 by_expert.setdefault(e, []).append((i, s))
-    y = {}
+    y, yb = {}, {}
     for e in sorted(by_expert):
         rows = by_expert[e]
-        ye = expert_mlp(x[[i for i, _ in rows]], *get(e), act=act)
+        res = expert_mlp(x[[i for i, _ in rows]], *get(e), act=act, with_spread=with_spread)
+        ye, be = res if with_spread else (res, None)
         for j, key in enumerate(rows):
             y[key] = ye[j]
+            if with_spread:
+                yb[key] = be[j]
 
     acc = np.zeros((len(sel), hidden), dtype=np.float64)
+    bound = np.zeros_like(acc)
     for i, t in enumerate(sel):
         for s in range(k):                            # ascending slot order
             if (i, s) in y:
                 acc[i] += wts[t, s] * y[(i, s)]
-    return acc
+                if with_spread:
+                    bound[i] += abs(wts[t, s]) * yb[(i, s)]
+    return (acc, bound) if with_spread else acc
