@@ -4,24 +4,28 @@
 // block scales inside the instruction (the OCP MX product; the MXFP8 x MXFP4
 // variant of the grouped GEMM).
 //
-// Work item = (128-row tile of one expert's rows, 256-column slice of the
+// Work item = (128-row tile of one expert's rows, slice of 16 * kWaves * 2
 // weight rows).  The weights are what the batch streams from HBM (an expert
 // holds 23.4 MB of codes and scales at hidden 7168 / intermediate 2048, while
 // its ~85 routed rows of E4M3 activations hold 0.6 MB), so one tile covers
 // every row an expert has in a balanced batch and each weight byte is read
-// once.  A workgroup of eight waves (two per SIMD, one workgroup per CU) runs
-// one stage per 128-K column block:
+// once.  A workgroup of kWaves waves (four by default: two workgroups per CU,
+// whose stage barriers fall at different times) runs one stage per 128-K
+// column block:
 //  * weights: the repacked 1 KB tile is already the MFMA's B operand (lane l
 //    holds the 32 codes of row l%16, K group l/16), so each wave loads its two
 //    row blocks straight into registers, kDepth stages ahead, with their E8M0
 //    bytes (buffer loads: one VGPR offset, SGPR bases);
 //  * activations: the tile's rows (gathered through the route permutation
-//    for FC1) are shared by the eight waves, so they and their E8M0 bytes are
-//    copied global->LDS by buffer_load ... lds, kDepth stages ahead, into
-//    128-byte rows under the same conflict-free chunk swizzle as the bf16
-//    prefill kernel; each lane reads its A operand (bytes 16(l/16).. and
-//    64+16(l/16).. of row l%16) with two ds_read_b128 and its scale byte
-//    (K group l/16) with one ds_read_u8.
+//    for FC1) are shared by the waves, so they are copied global->LDS by
+//    buffer_load ... lds, kDepth stages ahead, into 128-byte rows under the
+//    same conflict-free chunk swizzle as the bf16 prefill kernel; each lane
+//    reads its A operand (bytes 16(l/16).. and 64+16(l/16).. of row l%16)
+//    with two ds_read_b128.  Their E8M0 bytes (K/32 per row, 28 KB per tile
+//    at hidden 7168, dynamic LDS) are copied once per tile with whole-row
+//    dword requests, and each lane reads its byte (K group l/16) with one
+//    ds_read_u8: per-stage copies of four bytes per row would cost a cache
+//    line request each.
 // Each wave owns all rows x 32 columns (one gate/up pair for FC1): 2*LIVE
 // 16-row blocks by two row blocks; 32-row blocks wholly past the tile's rows
 // are neither copied nor multiplied.
@@ -40,14 +44,21 @@ namespace {
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 
+#ifndef MOE_MX_WAVES
+#define MOE_MX_WAVES 4
+#endif
 constexpr int kRows = kPrefillMxRows;       // rows per tile
-constexpr int kWaves = 8;
+constexpr int kWaves = MOE_MX_WAVES;        // 8: one workgroup per CU; 4: two
 constexpr int kNBW = 2;                     // row blocks (16 output columns each) per wave
-constexpr int kBlocks = kWaves * kNBW;      // per workgroup: 256 output columns
-constexpr int kDepth = 3;                   // stages loaded ahead of the one multiplied
+constexpr int kBlocks = kWaves * kNBW;      // output columns per workgroup / 16
+constexpr int kCopySlots = 16 / kWaves;     // 8-row activation copies per wave and stage, at most
+static_assert(kWaves == 4 || kWaves == 8, "four or eight waves per workgroup");
+#ifndef MOE_MX_DEPTH
+#define MOE_MX_DEPTH 2
+#endif
+constexpr int kDepth = MOE_MX_DEPTH;        // stages loaded ahead of the one multiplied
 constexpr int kBufs = kDepth + 1;           // LDS stage buffers
 constexpr int kStageBytes = kRows * kTileK;   // 128 rows x 128 E4M3
-constexpr int kStageScaleBytes = kRows * 4;   // their four E8M0 bytes
 constexpr int kRsrcWord3 = 0x00020000;        // raw buffer, 32-bit data format
 
 // vmcnt <= n with lgkmcnt 0 (every LDS read of the previous stage returned)
@@ -56,22 +67,33 @@ constexpr int kRsrcWord3 = 0x00020000;        // raw buffer, 32-bit data format
 __device__ __forceinline__ int swz(int c, int r) { return c ^ (r & 7) ^ ((r >> 3) & 1); }
 
 // Wait until at most `ahead` stage groups of this wave's loads are still
-// outstanding; a group is na + B loads (na, ahead wave-uniform; s_waitcnt takes
-// an immediate, hence the cases).
+// outstanding; a group is NA + B loads (s_waitcnt takes an immediate, hence
+// the cases over the wave-uniform `ahead`).
+template <int B, int NA>
+__device__ __forceinline__ void wait_ahead(int ahead) {
+  switch (ahead) {
+    case 0: MOE_WAIT_VM_LGKM(0); break;
+    case 1: MOE_WAIT_VM_LGKM(1 * (NA + B)); break;
+    case 2: MOE_WAIT_VM_LGKM(2 * (NA + B)); break;
+    case 3: MOE_WAIT_VM_LGKM(3 * (NA + B)); break;
+    case 4: MOE_WAIT_VM_LGKM(4 * (NA + B)); break;
+    case 5: MOE_WAIT_VM_LGKM(5 * (NA + B)); break;
+    case 6: MOE_WAIT_VM_LGKM(6 * (NA + B)); break;
+    default: MOE_WAIT_VM_LGKM(7 * (NA + B)); break;
+  }
+}
 template <int B>
 __device__ __forceinline__ void wait_groups(int ahead, int na) {
-#define MOE_W(NA)                                         \
-  if (na == NA) {                                         \
-    if (ahead >= 2) MOE_WAIT_VM_LGKM(2 * (NA + B));       \
-    else if (ahead == 1) MOE_WAIT_VM_LGKM(NA + B);        \
-    else MOE_WAIT_VM_LGKM(0);                             \
-    return;                                               \
+  switch (na) {
+    case 0: wait_ahead<B, 0>(ahead); break;
+    case 1: wait_ahead<B, 1>(ahead); break;
+    case 2: wait_ahead<B, 2>(ahead); break;
+    case 3: wait_ahead<B, 3>(ahead); break;
+    default: wait_ahead<B, 4>(ahead); break;
   }
-  MOE_W(0) MOE_W(1) MOE_W(2)
-#undef MOE_W
-  MOE_WAIT_VM_LGKM(0);
 }
-static_assert(kDepth <= 3, "wait_groups covers up to two stage groups in flight behind the current one");
+static_assert(kDepth >= 1 && kDepth <= 8, "wait_ahead covers up to seven stage groups behind the current one");
+static_assert(7 * (kCopySlots + 2 * kNBW) <= 63, "vmcnt holds at most 63");
 
 template <bool FC1, int LIVE>
 __device__ __forceinline__ void tile_body(const FcArgs& a, uint8_t* sa, uint8_t* ss, int e, int row0, int rows,
@@ -90,25 +112,34 @@ __device__ __forceinline__ void tile_body(const FcArgs& a, uint8_t* sa, uint8_t*
       __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(a.a), (short)0, a.a_rows * a.lda, kRsrcWord3);
   const __amdgpu_buffer_rsrc_t rascl = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(a.a_scales), (short)0, a.a_rows * sgroups, kRsrcWord3);
-  // activation copies: group g (rows 8g .. 8g+7) is copied by wave g % 8; lane
-  // L fills row 8g + L/8 at chunk position L%8
-  const int na = (GROUPS - wave + kWaves - 1) / kWaves;   // this wave's groups: 0, 1 or 2
-  uint32_t aoff[2];
+  // activation copies: group g (rows 8g .. 8g+7) is copied by wave g % kWaves;
+  // lane L fills row 8g + L/8 at chunk position L%8
+  const int na = (GROUPS - wave + kWaves - 1) / kWaves;   // this wave's groups: 0 .. kCopySlots
+  uint32_t aoff[kCopySlots];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
+  for (int j = 0; j < kCopySlots; ++j) {
     const int r = 8 * (wave + kWaves * j) + (lane >> 3);
     const int rr = min(r, rows - 1);
     const int ar = FC1 ? a.perm[row0 + rr] / a.top_k : row0 + rr;
     aoff[j] = (uint32_t)ar * (uint32_t)a.lda + swz(lane & 7, r) * 16;
   }
-  // scale copy: lanes 0..15 each fill the dword of row 16 wave + L: its four
-  // E8M0 bytes of the stage, one per K group (rows are 4-byte aligned:
-  // sgroups is a multiple of 4)
-  uint32_t sofs;
+  // scale copy, once per tile: the live rows' E8M0 bytes, row-major with
+  // sgroups bytes per row (a multiple of 4), as 64-dword copies spread over
+  // the waves; lane L of copy i fills dword 64 i + L.  Issued before the
+  // first stage's loads, so the first stage's wait covers them.
   {
-    const int rr = min(16 * wave + (lane & 15), rows - 1);
-    const int ar = FC1 ? a.perm[row0 + rr] / a.top_k : row0 + rr;
-    sofs = (uint32_t)ar * (uint32_t)sgroups;
+    // rounded up: the last copy may run past the live rows (their bytes are
+    // never read; 32 LIVE sgroups is a multiple of 128, so it ends inside the
+    // 128 sgroups bytes of ss)
+    const int copies = (32 * LIVE * sgroups + 4 * kWave - 1) / (4 * kWave);
+    for (int i = wave; i < copies; i += kWaves) {
+      const int byte = 4 * (kWave * i + lane);
+      const int r = byte / sgroups;
+      const int rr = min(r, rows - 1);
+      const int ar = FC1 ? a.perm[row0 + rr] / a.top_k : row0 + rr;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rascl, (lds_void_t*)(ss + i * 4 * kWave), 4,
+                                               (uint32_t)ar * (uint32_t)sgroups + (byte - r * sgroups), 0, 0, 0);
+    }
   }
   // this wave's two weight row blocks, as buffer resources sized to them
   const int nb0 = slice * kBlocks + wave * kNBW;
@@ -131,13 +162,10 @@ __device__ __forceinline__ void tile_body(const FcArgs& a, uint8_t* sa, uint8_t*
   auto issue_lds = [&](int s) {
     uint8_t* buf = sa + (s % kBufs) * kStageBytes;
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < kCopySlots; ++j)
       if (j < na)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(racts, (lds_void_t*)(buf + (wave + kWaves * j) * 1024), 16,
                                                  aoff[j], s * kTileK, 0, 0);
-    if (lane < 16)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rascl, (lds_void_t*)(ss + (s % kBufs) * kStageScaleBytes + wave * 64),
-                                               4, sofs, 4 * s, 0, 0);
   };
   auto load_regs = [&](u32x4_t (&q)[kNBW], uint32_t (&sb)[kNBW], int s) {
 #pragma unroll
@@ -153,7 +181,7 @@ __device__ __forceinline__ void tile_body(const FcArgs& a, uint8_t* sa, uint8_t*
   const int rl = lane & 15, q = lane >> 4;
   const int lo_off = rl * kTileK + swz(q, rl) * 16;
   const int hi_off = rl * kTileK + swz(4 + q, rl) * 16;
-  const int s_off = rl * 4 + q;
+  const int s_off = rl * sgroups + q;
 
 #pragma unroll
   for (int d = 0; d < kDepth; ++d)
@@ -170,18 +198,18 @@ __device__ __forceinline__ void tile_body(const FcArgs& a, uint8_t* sa, uint8_t*
         // this wave's loads of stage st have landed (those of the stages after
         // it may still be in flight) and its LDS reads of stage st-1 have
         // returned; the barrier extends both to every wave
-        wait_groups<1 + 2 * kNBW>(min(kDepth - 1, S - 1 - st), na);
+        wait_groups<2 * kNBW>(min(kDepth - 1, S - 1 - st), na);
         asm volatile("" ::: "memory");
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
         if (st + kDepth < S) issue_lds(st + kDepth);   // into the buffers of stage st-1
         const uint8_t* cur = sa + (st % kBufs) * kStageBytes;
-        const uint8_t* curs = ss + (st % kBufs) * kStageScaleBytes;
+        const uint8_t* curs = ss + 4 * st;
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
           const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(cur + mb * 16 * kTileK + lo_off);
           const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(cur + mb * 16 * kTileK + hi_off);
-          const int sc = curs[mb * 64 + s_off];
+          const int sc = curs[mb * 16 * sgroups + s_off];
           const i32x8_t Af = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
                               (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
 #pragma unroll
@@ -215,9 +243,9 @@ __device__ __forceinline__ void tile_body(const FcArgs& a, uint8_t* sa, uint8_t*
 }
 
 template <bool FC1>
-__global__ __launch_bounds__(kWaves * kWave, 1) void fc_pre_mx(FcArgs a, int slices) {
+__global__ __launch_bounds__(kWaves * kWave, 8 / kWaves) void fc_pre_mx(FcArgs a, int slices) {
   __shared__ __align__(1024) uint8_t sa[kBufs * kStageBytes];
-  __shared__ __align__(16) uint8_t ss[kBufs * kStageScaleBytes];
+  extern __shared__ __align__(16) uint8_t ss[];   // kRows * K/32 bytes (launch size)
   const int ntiles = *a.tile_count;
   const int total = ntiles * slices;
   // eight contiguous chunks of the (tile, slice) list, one per XCD
@@ -242,7 +270,8 @@ hipError_t launch(const FcArgs& a, int tiles_max, hipStream_t stream) {
   const int slices = a.mat.nb / kBlocks;
   const long long items = (long long)tiles_max * slices;
   const long long grid = (items + 7) / 8 * 8;
-  hipLaunchKernelGGL((fc_pre_mx<FC1>), dim3((unsigned)grid), dim3(kWaves * kWave), 0, stream, a, slices);
+  const size_t scale_bytes = (size_t)kRows * (a.lda / 32);
+  hipLaunchKernelGGL((fc_pre_mx<FC1>), dim3((unsigned)grid), dim3(kWaves * kWave), scale_bytes, stream, a, slices);
   return hipGetLastError();
 }
 

@@ -40,7 +40,7 @@ size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
 
-constexpr int32_t kMaxDim = 16384;
+constexpr int32_t kMaxDim = moe::kMaxDimension;
 constexpr int32_t kMaxExperts = 1024;
 constexpr int32_t kMaxTopK = 32;
 constexpr int64_t kMaxRoutes = 262144;

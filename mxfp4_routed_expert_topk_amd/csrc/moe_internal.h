@@ -30,6 +30,7 @@ constexpr int kTileBytes = 1024;    // codes per tile
 constexpr int kScaleGroupBytes = 256;
 constexpr int kRouteChunk = 1024;   // routes per route workgroup
 constexpr int kBM = 16;             // rows per FC tile (one MFMA M block)
+constexpr int kMaxDimension = 16384;  // largest hidden / intermediate size a plan accepts
 
 struct MatLayout {
   int32_t n, k;        // logical rows / columns
