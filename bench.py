@@ -1,6 +1,7 @@
 """Benchmark of the MXFP4 routed-expert MoE layer on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--m 128] [--no-extra] [--no-cpu]
+                    [--workload decode|prefill1536|fusedsum4096|mxfp8x4096]
 
 A step is one moe_mxfp4_forward call (route -> FC1 -> FC2 -> combine) over one
 batch of the decode workload: hidden 7168, intermediate 2048, 224 resident of
@@ -11,7 +12,13 @@ routing/activation sets are rotated so consecutive steps touch different
 experts (small-M working sets would otherwise stay in the 256 MB last-level
 cache between steps).
 
-Prints ONE JSON line: whole-job tokens/s (`value`); the roofline of the
+--workload picks a single prefill configuration instead (1536 tokens uniform,
+4096 tokens Zipf fused-sum, 4096 tokens MXFP8), for profiling one workload at a
+time: its tokens/s is the value and its FC1 kernel is priced against the MFMA
+peak of its dtype (extras and the CPU baseline are skipped).
+
+Prints ONE JSON line: whole-job tokens/s (`value`, eager launches; the same
+steps replayed from captured hipGraphs are reported beside it); the roofline of the
 dominant kernel (FC1), timed with HIP events recorded on the launch stream
 right before and after that kernel in a second pass over the same steps; the layer's own
 HBM fraction; extra entries for the other decode batch sizes and the prefill
@@ -133,7 +140,35 @@ class Batches:
         alg = np.array([self.per_step(warmup + j) for j in range(steps)])
         return {"ms_per_step": ms, "ms_per_step_with_events": float(stage.sum(axis=1).mean()),
                 "stage_ms": stage.mean(axis=0), "fc1_ms": stage[:, 1],
-                "layer_bytes": alg[:, 0].mean(), "fc1_bytes": alg[:, 1].mean(), "flops": alg[:, 2].mean()}
+                "layer_bytes": alg[:, 0].mean(), "fc1_bytes": alg[:, 1].mean(), "flops": alg[:, 2].mean(),
+                "graph_ms_per_step": self.run_graph(steps, warmup)}
+
+    def run_graph(self, steps, warmup):
+        """The same steps replayed from one captured hipGraph per input set (the
+        forward enqueues only kernels, so it captures as is): the per-launch
+        host and queue gaps drop out, as in a serving loop."""
+        import torch
+        graphs = []
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for x, ids, wts in self.inputs:
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=side):
+                    self.plan.forward(x, ids, wts, out=self.out, acc=self.acc)
+                graphs.append(g)
+        torch.cuda.current_stream().wait_stream(side)
+        for j in range(warmup):
+            graphs[j % len(graphs)].replay()
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record()
+        for j in range(steps):
+            graphs[(warmup + j) % len(graphs)].replay()
+        end.record()
+        torch.cuda.synchronize()
+        del graphs
+        return start.elapsed_time(end) / steps
 
     def summary(self, r):
         ms = r["ms_per_step"]
@@ -145,20 +180,32 @@ class Batches:
                 "tflops": round(tflops, 2), "mfma_frac": round(tflops / peak, 4),
                 "mfma_peak_tflops": peak,
                 "stage_us": {k: round(float(v) * 1e3, 2) for k, v in zip(STAGES, r["stage_ms"])},
-                "us_per_step_with_stage_events": round(r["ms_per_step_with_events"] * 1e3, 2)}
+                "us_per_step_with_stage_events": round(r["ms_per_step_with_events"] * 1e3, 2),
+                "graph_us_per_step": round(r["graph_ms_per_step"] * 1e3, 2),
+                "graph_tokens_per_s": round(self.T / (r["graph_ms_per_step"] * 1e-3), 1)}
 
 
-def counter_traffic():
+# FC1 kernel source of each workload (the counter records hash it with the shared header)
+FC1_SOURCE = {"decode": "gemm.hip", "prefill1536": "gemm_prefill.hip", "fusedsum4096": "gemm_prefill.hip",
+              "mxfp8x4096": "gemm_prefill_mx.hip"}
+PREFILL = {"prefill1536": 2, "fusedsum4096": 3, "mxfp8x4096": 4}
+
+
+def source_hash(workload):
+    import hashlib
+    csrc = os.path.join(ROOT, "mxfp4_routed_expert_topk_amd", "csrc")
+    src = b"".join(open(os.path.join(csrc, f), "rb").read() for f in (FC1_SOURCE[workload], "moe_internal.h"))
+    return hashlib.sha256(src).hexdigest()
+
+
+def counter_traffic(workload, tag):
     """HBM bytes per FC1 launch from the committed rocprofv3 counter runs, or None
     when the kernel sources changed since those counters were taken."""
-    import hashlib
-    path = os.path.join(ROOT, "profiles", "fc1_decode_m128_traffic.json")
+    path = os.path.join(ROOT, "profiles", f"fc1_{tag}_traffic.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    csrc = os.path.join(ROOT, "mxfp4_routed_expert_topk_amd", "csrc")
-    src = b"".join(open(os.path.join(csrc, f), "rb").read() for f in ("gemm.hip", "moe_internal.h"))
-    if hashlib.sha256(src).hexdigest() != rec.get("source_sha256"):
+    if source_hash(workload) != rec.get("source_sha256"):
         return None
     return rec["hbm_bytes_per_dispatch"]
 
@@ -184,6 +231,42 @@ def cpu_baseline():
                       f"matmuls on {threads} BLAS threads"}
 
 
+def prefill_line(args):
+    """The JSON line of one prefill configuration (see --workload)."""
+    import workloads as W
+    cid = PREFILL[args.workload]
+    case = W.config_case(cid)
+    pl, _ = build_plan(cid, case.shape.tokens)
+    b = Batches(pl, cid, None, 2)
+    r = b.run(args.steps, args.warmup)
+    summ = b.summary(r)
+    mx = case.act == "mxfp8"
+    s = case.shape
+    valid = float(np.mean(b.valid))
+    fc1_us = float(np.mean(r["fc1_ms"])) * 1e3
+    fc1_tflops = 2.0 * valid * s.hidden * 2 * s.inter / (fc1_us * 1e-6) / 1e12
+    peak = FP8_PEAK_TFLOPS if mx else BF16_PEAK_TFLOPS
+    tag = f"{args.workload}"
+    line = {
+        "metric": METRIC, "value": summ["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(r["ms_per_step"], 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "fp8xfp4" if mx else "bf16", "data": "synthetic",
+        "config": {"workload": f"{args.workload}: {s.tokens} tokens, hidden {s.hidden}, intermediate {s.inter}, "
+                               f"{s.experts} experts, top-{s.top_k}, {W.CONFIGS[cid]['routing']} routing, "
+                               f"{'MXFP8' if mx else 'bf16'} activations, MXFP4 weights",
+                   "tokens": s.tokens, "hidden": s.hidden, "intermediate": s.inter, "experts_resident": s.experts,
+                   "top_k": s.top_k},
+        "roofline": {"bound": "mfma", "achieved": round(fc1_tflops, 1), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(fc1_tflops / peak, 4), "traffic": counter_traffic(args.workload, tag),
+                     "kernel": ("fc_pre_mx<true> (FC1, MXFP8)" if mx else "fc_pre<true,128> (FC1, bf16)"),
+                     "kernel_us": round(fc1_us, 2),
+                     "alg_flops_per_launch": 2.0 * valid * s.hidden * 2 * s.inter},
+        "layer": summ,
+    }
+    pl.close()
+    return line
+
+
 def main():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
@@ -193,6 +276,7 @@ def main():
     p.add_argument("--sets", type=int, default=8)
     p.add_argument("--no-extra", action="store_true")
     p.add_argument("--no-cpu", action="store_true")
+    p.add_argument("--workload", default="decode", choices=["decode"] + list(PREFILL))
     p.add_argument("--copy-probe", action="store_true",
                    help="first copy 512 MiB with torch three times: a kernel of known bytes for counter scaling")
     args = p.parse_args()
@@ -215,6 +299,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    if args.workload != "decode":
+        print(json.dumps(prefill_line(args)), flush=True)
+        return
     plan, _ = build_plan(1, max(max(W.DECODE_M), args.m))
     head_b = Batches(plan, 1, args.m, args.sets)
     r = head_b.run(args.steps, args.warmup)
@@ -241,8 +328,8 @@ def main():
                    "experts_global": 384, "top_k": 8},
         "roofline": {"bound": "hbm", "achieved": round(fc1_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(fc1_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": counter_traffic() if args.m == 128 else None,
-                     "kernel": "fc_m16<FC1,bf16>", "kernel_us": round(fc1_us, 2),
+                     "traffic": counter_traffic("decode", "decode_m128") if args.m == 128 else None,
+                     "kernel": "fc_dec<true,false,4,4,2> (FC1, bf16, 16-row tiles)", "kernel_us": round(fc1_us, 2),
                      "alg_bytes_per_launch": int(r["fc1_bytes"])},
         "layer": head,
     }
