@@ -9,6 +9,7 @@ Contents, each written from the definition on the pages (citations in each
 module):
   formats  E2M1 / E8M0 / E4M3FN / bfloat16 codecs, MXFP4 dequantisation
   route    per-expert counts, offsets, stable permutation (two formulations)
+  router   router top-k ids and softmax route weights from logits (upstream of the layer)
   moe      fp64 forward of the layer, MXFP8 activation quantisation
   brute    scalar-loop brute force for tiny shapes
   compare  the acceptance rule (3 bf16 ULP or 4e-3 row relative L2)
@@ -22,6 +23,7 @@ from .formats import (E2M1_MAGNITUDES, E4M3_MAX, bf16_bits_to_f64, dequant_mxfp4
                       e4m3_encode, e4m3_value, e8m0_value, f32_to_bf16_rne, pack_nibbles,
                       ulp_bf16, unpack_nibbles, validate_scale_bytes)
 from .route import route_sort, route_sort_by_key
+from .router import router_topk, router_topk_np
 from .moe import (expert_mlp, forward, fp32_dot_bound, mxfp8_dequantize, mxfp8_quantize,
                   mxfp8_roundtrip, mxfp8_roundtrip_spread, mxfp8_scale_exponent, silu)
 from .compare import check_rows, rel_l2
