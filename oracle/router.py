@@ -11,8 +11,8 @@ gather/router path).  Reading taken, the one the workloads' "top-k softmax"
 routing uses:
 
   * ids: the k experts with the largest logits, in descending order; equal
-    logits rank the lower expert id first; a NaN logit ranks below every
-    number (as -inf, ties again by id);
+    logits rank the lower expert id first; a NaN logit counts as -inf (in the
+    ranking, ties again by id, and in the weights, where it gets 0);
   * weights: softmax over the k selected logits, max-subtracted:
         w_s = exp(l_s - l_0) / sum_{j=0..k-1} exp(l_j - l_0)
     with the sum taken over slots in ascending order.
@@ -45,7 +45,7 @@ def router_topk(logits: np.ndarray, k: int):
         row = [float(v) for v in lg[t]]
         order = sorted(range(e_all), key=lambda e: (-_rank_value(row[e]), e))[:k]
         ids[t] = order
-        sel = [row[e] for e in order]
+        sel = [_rank_value(row[e]) for e in order]
         top = sel[0]
         ex = [math.exp(v - top) if not math.isnan(v - top) else math.nan for v in sel]
         total = 0.0

@@ -15,9 +15,12 @@ def test_hand_example_with_ties_and_nan():
     e = [1.0, math.exp(-1.0), math.exp(-1.0), math.exp(-2.5), math.exp(-2.5)]
     s = sum(e)
     np.testing.assert_allclose(w[0], [v / s for v in e], rtol=0, atol=1e-15)
-    # the NaN ranks below -inf? no: both rank as -inf and the lower id (4) comes first
-    ids8, _ = router_topk(lg, 8)
+    # NaN and -inf both count as -inf: the lower id (4) first, and both weigh 0
+    ids8, w8 = router_topk(lg, 8)
     assert ids8[0, 6:].tolist() == [4, 7]
+    assert w8[0, 6] == 0.0 and w8[0, 7] == 0.0
+    np.testing.assert_allclose(w8[0, :5], w[0], rtol=0, atol=1e-15)
+    np.testing.assert_allclose(router_topk_np(lg, 8)[1], w8, rtol=1e-13, atol=0)
 
 
 def test_two_formulations_agree():
