@@ -15,11 +15,13 @@ def test_hand_example_with_ties_and_nan():
     e = [1.0, math.exp(-1.0), math.exp(-1.0), math.exp(-2.5), math.exp(-2.5)]
     s = sum(e)
     np.testing.assert_allclose(w[0], [v / s for v in e], rtol=0, atol=1e-15)
-    # NaN and -inf both count as -inf: the lower id (4) first, and both weigh 0
+    # NaN and -inf both count as -inf: the lower id (4) first, and both weigh 0;
+    # the six finite logits (the five above and -1.0 at id 2) share the weight
     ids8, w8 = router_topk(lg, 8)
-    assert ids8[0, 6:].tolist() == [4, 7]
+    assert ids8[0].tolist() == [6, 1, 3, 0, 5, 2, 4, 7]
     assert w8[0, 6] == 0.0 and w8[0, 7] == 0.0
-    np.testing.assert_allclose(w8[0, :5], w[0], rtol=0, atol=1e-15)
+    e6 = e + [math.exp(-4.0)]
+    np.testing.assert_allclose(w8[0, :6], [v / sum(e6) for v in e6], rtol=0, atol=1e-15)
     np.testing.assert_allclose(router_topk_np(lg, 8)[1], w8, rtol=1e-13, atol=0)
 
 
