@@ -231,6 +231,32 @@ def cpu_baseline():
                       f"matmuls on {threads} BLAS threads"}
 
 
+def router_timings(reps=200):
+    """moe_router_topk alone: microseconds per call at the pages' expert counts and
+    batch buckets (logits resident in HBM, back-to-back calls)."""
+    import torch
+    import mxfp4_routed_expert_topk_amd as moe
+    import workloads as W
+    from workloads import device as D
+    res = {}
+    for T, E, k in ((1, 224, 8), (128, 224, 8), (128, 896, 16), (4096, 224, 8), (4096, 896, 16)):
+        lg = D.to_dev(W.gen_logits(7, T, E))
+        ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+        w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+        for _ in range(10):
+            moe.router_topk(lg, k, ids, w)
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record()
+        for _ in range(reps):
+            moe.router_topk(lg, k, ids, w)
+        end.record()
+        torch.cuda.synchronize()
+        us = start.elapsed_time(end) / reps * 1e3
+        res[f"T{T}_E{E}_k{k}"] = {"us": round(us, 2), "logit_gbs": round(T * E * 4 / (us * 1e-6) / 1e9, 1)}
+    return res
+
+
 def prefill_line(args):
     """The JSON line of one prefill configuration (see --workload)."""
     import workloads as W
@@ -353,6 +379,8 @@ def main():
             pl.close()
             del pl, b
             torch.cuda.empty_cache()
+        extra["router_topk"] = router_timings()
+        log(f"router: {extra['router_topk']}")
         line["extra"] = extra
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline()

@@ -134,6 +134,27 @@ moe_status moe_mxfp4_route(moe_mxfp4_plan_t plan, const int32_t* topk_ids, int32
 moe_status moe_mxfp8_quantize(const uint16_t* x_bf16, int32_t rows, int32_t cols,
                               uint8_t* codes, uint8_t* scales, hipStream_t stream);
 
+/* Router top-k upstream of the layer: the topk_ids / topk_weights that
+ * moe_mxfp4_forward consumes, from fp32 router logits [num_tokens, num_experts]
+ * (row-major).  The contract follows the pages (pegainfer PR #867, commit
+ * b49a9f04: batched router top-k over E in {224, 896}; b12x PR #339: top-16
+ * kept in registers, a fixed tie order, a sequential fp32 normalisation of
+ * the route weights); the scoring function is not on the pages and the
+ * reading taken is the top-k softmax:
+ *   topk_ids     [num_tokens, top_k] int32: the top_k largest logits of the
+ *                row in descending order; equal logits rank the lower expert
+ *                id first; a NaN logit counts as -inf (ranked last, weight 0);
+ *   topk_weights [num_tokens, top_k] fp32: exp(l_s - l_0) / sum_j exp(l_j - l_0)
+ *                over the selected logits l_0 >= l_1 >= ..., exp in fp32, the
+ *                sum over slots in ascending order.
+ * Ids are exact; weights are within a few fp32 rounding steps of the exact
+ * softmax.  Requires 1 <= num_experts <= 1024 and 1 <= top_k <= min(32,
+ * num_experts); num_tokens = 0 is a no-op.  Pointers are device memory,
+ * 16-byte aligned; nothing is allocated; the call only enqueues on stream. */
+moe_status moe_router_topk(const float* logits, int32_t num_tokens, int32_t num_experts,
+                           int32_t top_k, int32_t* topk_ids, float* topk_weights,
+                           hipStream_t stream);
+
 /* Record one event at each stage boundary of subsequent forward calls of this
  * plan: events[0] before the first kernel, then after route, FC1, FC2 and the
  * combine (n = 5).  Pass n = 0 to stop.  The events are owned by the caller

@@ -12,6 +12,7 @@ Names follow the C ABI in include/moe_mxfp4.h:
   Plan.forward(hidden, topk_ids, topk_weights, out=None, acc=None)
   Plan.route(topk_ids)                  -> (counts, offsets, perm, rowpos)
   mxfp8_quantize(x_bf16)                -> (codes, scales)
+  router_topk(logits, k)                -> (topk_ids, topk_weights)  (moe_router_topk)
 """
 from __future__ import annotations
 
@@ -28,7 +29,8 @@ MOE_ACT_MXFP8 = 1
 STATUS_NAMES = {0: "MOE_OK", 1: "MOE_ERR_ARG", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_ALIGN", 4: "MOE_ERR_CAPACITY",
                 5: "MOE_ERR_SCALE_BYTE", 6: "MOE_ERR_WORKSPACE", 7: "MOE_ERR_UNSUPPORTED", 8: "MOE_ERR_HIP"}
 EXPORTS = ("moe_mxfp4_query_sizes", "moe_mxfp4_plan", "moe_mxfp4_forward", "moe_mxfp4_route",
-           "moe_mxfp8_quantize", "moe_mxfp4_set_stage_events", "moe_mxfp4_destroy", "moe_mxfp4_last_error")
+           "moe_mxfp8_quantize", "moe_router_topk", "moe_mxfp4_set_stage_events", "moe_mxfp4_destroy",
+           "moe_mxfp4_last_error")
 
 
 class MoeError(RuntimeError):
@@ -75,6 +77,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_mxfp4_forward.argtypes = [vp, vp, vp, vp, i32, vp, vp, vp, sz, vp]
     lib.moe_mxfp4_route.argtypes = [vp, vp, i32, vp, vp, vp, vp, vp, sz, vp]
     lib.moe_mxfp8_quantize.argtypes = [vp, i32, i32, vp, vp, vp]
+    lib.moe_router_topk.argtypes = [vp, i32, i32, i32, vp, vp, vp]
     lib.moe_mxfp4_set_stage_events.argtypes = [vp, ctypes.POINTER(vp), i32]
     lib.moe_mxfp4_destroy.argtypes = [vp]
     lib.moe_mxfp4_destroy.restype = None
@@ -177,6 +180,17 @@ class Plan:
         arr = (ctypes.c_void_p * len(events))(*[ev.cuda_event for ev in events])
         self._events = (events, arr)   # keep alive while set
         _check(lib.moe_mxfp4_set_stage_events(self._h, arr, len(events)))
+
+
+def router_topk(logits, top_k, ids=None, weights=None, stream=None):
+    """topk_ids int32 [T, k] and topk_weights fp32 [T, k] from fp32 logits [T, E]
+    (moe_router_topk)."""
+    import torch
+    T, E = logits.shape
+    ids = torch.empty((T, top_k), dtype=torch.int32, device=logits.device) if ids is None else ids
+    weights = torch.empty((T, top_k), dtype=torch.float32, device=logits.device) if weights is None else weights
+    _check(load_library().moe_router_topk(_ptr(logits), T, E, top_k, _ptr(ids), _ptr(weights), _stream(stream)))
+    return ids, weights
 
 
 def mxfp8_quantize(x_bf16, stream=None):

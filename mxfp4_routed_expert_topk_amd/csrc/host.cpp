@@ -359,6 +359,25 @@ moe_status moe_mxfp8_quantize(const uint16_t* x, int32_t rows, int32_t cols, uin
   return ok();
 }
 
+moe_status moe_router_topk(const float* logits, int32_t T, int32_t E, int32_t k, int32_t* ids, float* weights,
+                           hipStream_t stream) {
+  if (T < 0) return fail(MOE_ERR_ARG, "num_tokens must be >= 0, got %d", T);
+  if (E < 1 || E > moe::kRouterMaxExperts)
+    return fail(MOE_ERR_SHAPE, "num_experts must be in [1, %d], got %d", moe::kRouterMaxExperts, E);
+  if (k < 1 || k > kMaxTopK || k > E)
+    return fail(MOE_ERR_SHAPE, "top_k must be in [1, min(%d, num_experts=%d)], got %d", kMaxTopK, E, k);
+  if (T == 0) return ok();
+  const void* ptrs[] = {logits, ids, weights};
+  const char* names[] = {"logits", "topk_ids", "topk_weights"};
+  for (int i = 0; i < 3; ++i) {
+    if (!ptrs[i]) return fail(MOE_ERR_ARG, "%s is null", names[i]);
+    if (misaligned(ptrs[i])) return fail(MOE_ERR_ALIGN, "%s must be 16-byte aligned, got %p", names[i], ptrs[i]);
+  }
+  hipError_t e = moe::launch_router_topk(logits, T, E, k, ids, weights, stream);
+  if (e != hipSuccess) return hip_fail(e, "router launch");
+  return ok();
+}
+
 moe_status moe_mxfp4_set_stage_events(moe_mxfp4_plan_t p, hipEvent_t* events, int32_t n) {
   if (!p) return fail(MOE_ERR_ARG, "plan is null");
   if (n != 0 && n != 5) return fail(MOE_ERR_ARG, "stage events: n must be 0 or 5, got %d", n);

@@ -120,6 +120,11 @@ constexpr int kPrefillMxRows = 128;
 hipError_t launch_fc1_prefill_mx(const FcArgs& a, int tiles_max, hipStream_t stream);
 hipError_t launch_fc2_prefill_mx(const FcArgs& a, int tiles_max, hipStream_t stream);
 
+// Router top-k (E <= kRouterMaxExperts, k <= 32).
+constexpr int kRouterMaxExperts = 1024;
+hipError_t launch_router_topk(const float* logits, int32_t T, int32_t E, int32_t k, int32_t* ids, float* weights,
+                              hipStream_t stream);
+
 hipError_t launch_combine(const float* y, const int32_t* rowpos, const int32_t* ids,
                           const float* w, int32_t T, int32_t k, int32_t H, int32_t E,
                           float* acc, uint16_t* out, hipStream_t stream);

@@ -382,6 +382,39 @@ def test_scale_byte_validation(byte, act, bad):
 
 
 # ------------------------------------------------------------------ MXFP8 activation quantiser
+# ------------------------------------------------------------------ router top-k (upstream of the layer)
+ROUTER_CASES = [(1, 224, 8, False, False), (128, 896, 16, False, False), (128, 224, 16, True, False),
+                (1000, 1024, 32, True, True), (37, 5, 5, False, True), (64, 64, 1, True, False),
+                (3, 896, 16, False, True)]
+
+
+@pytest.mark.parametrize("T,E,k,ties,specials", ROUTER_CASES)
+def test_router_topk(T, E, k, ties, specials):
+    say(f"router T={T} E={E} k={k} ties={ties} specials={specials}")
+    lg = W.gen_logits(60 + T + E + k, T, E, ties=ties, specials=specials)
+    ids, w = moe.router_topk(G.to_dev(lg), k)
+    torch.cuda.synchronize()
+    ref_ids, ref_w = oracle.router_topk(lg, k)
+    np.testing.assert_array_equal(ids.cpu().numpy(), ref_ids)
+    # fp32 subtraction, expf and the slot-order sum against the fp64 definition
+    np.testing.assert_allclose(w.cpu().numpy(), ref_w, rtol=4e-6, atol=1e-12)
+
+
+def test_router_feeds_the_layer():
+    """Device router -> device forward, against oracle router -> oracle forward on
+    the same logits (ids identical, weights within fp32 rounding)."""
+    shape = W.LayerShape(24, 256, 128, 8, 8, 4)
+    base = W.make_case("routed", shape, 61)
+    lg = W.gen_logits(62, 24, 8)
+    ids, w = moe.router_topk(G.to_dev(lg), 4)
+    dev_case = W.Case(base.name, shape, base.seed, base.hidden_bits, ids.cpu().numpy(), w.cpu().numpy(), 120, 130)
+    ref_ids, ref_w = oracle.router_topk(lg, 4)
+    ref_case = W.Case(base.name, shape, base.seed, base.hidden_bits, ref_ids, ref_w.astype(np.float32), 120, 130)
+    plan, _ = G.make_plan(dev_case)
+    out, acc = G.run_forward(plan, dev_case)
+    check_layer(ref_case, out, acc, ew=ref_case.experts())
+
+
 def test_mxfp8_quantize_bitexact():
     say("mxfp8 quantiser")
     case = W.config_case(4)

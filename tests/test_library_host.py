@@ -105,5 +105,18 @@ def test_quantize_argument_errors(lib):
     assert lib.moe_mxfp8_quantize(16, 0, 64, 16, 16, None) == 0     # empty is a no-op
 
 
+def test_router_argument_errors(lib):
+    assert lib.moe_router_topk(16, 4, 0, 1, 16, 16, None) == 2
+    assert b"num_experts must be in [1, 1024], got 0" in lib.moe_mxfp4_last_error()
+    assert lib.moe_router_topk(16, 4, 1025, 8, 16, 16, None) == 2
+    assert lib.moe_router_topk(16, 4, 8, 9, 16, 16, None) == 2
+    assert b"top_k must be in [1, min(32, num_experts=8)], got 9" in lib.moe_mxfp4_last_error()
+    assert lib.moe_router_topk(16, 4, 896, 33, 16, 16, None) == 2
+    assert lib.moe_router_topk(16, -1, 8, 2, 16, 16, None) == 1
+    assert lib.moe_router_topk(None, 4, 8, 2, 16, 16, None) == 1
+    assert lib.moe_router_topk(16, 4, 8, 2, 16, 24, None) == 3
+    assert lib.moe_router_topk(16, 0, 8, 2, 16, 16, None) == 0       # no tokens: a no-op
+
+
 def test_destroy_null_is_a_noop(lib):
     lib.moe_mxfp4_destroy(None)

@@ -43,6 +43,7 @@ __all__ = [
     "make_case",
     "gen_hidden",
     "gen_routes",
+    "gen_logits",
     "gen_expert",
     "gen_experts",
 ]
@@ -144,6 +145,22 @@ def gen_routes(seed: int, tokens: int, top_k: int, experts: int, experts_global:
         hi = max(experts_global, experts + 1)
         flat[where[half:]] = rng.integers(experts, hi, size=nbad - half, dtype=np.int32)
     return np.ascontiguousarray(ids), np.ascontiguousarray(w.astype(np.float32))
+
+
+def gen_logits(seed: int, tokens: int, experts: int, ties: bool = False, specials: bool = False):
+    """Router logits fp32 [T, E]: N(0,1); ``ties`` rounds them to multiples of
+    1/4 (many exact ties); ``specials`` sets about 2% of them to NaN or -inf."""
+    rng = _rng(seed, 5)
+    lg = rng.standard_normal((tokens, experts), dtype=np.float32)
+    if ties:
+        lg = (np.round(lg * 4) / 4).astype(np.float32)
+    if specials and lg.size:
+        n = max(1, lg.size // 50)
+        flat = lg.reshape(-1)
+        where = rng.choice(lg.size, size=n, replace=False)
+        flat[where[: n // 2]] = np.nan
+        flat[where[n // 2:]] = -np.inf
+    return np.ascontiguousarray(lg)
 
 
 def gen_expert(seed: int, e: int, hidden: int, inter: int, scale_lo: int, scale_hi: int):
