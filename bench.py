@@ -198,6 +198,31 @@ def source_hash(workload):
     return hashlib.sha256(src).hexdigest()
 
 
+class K3Batches(Batches):
+    """Input sets of the K3-shape decode workload at M tokens (see workloads.k3_case)."""
+
+    def __init__(self, plan, m, sets):
+        import torch
+        import workloads as W
+        from workloads import device as D
+        self.plan = plan
+        base = W.k3_case(m)
+        self.base = base
+        s = base.shape
+        self.T, self.H, self.I, self.E, self.k = s.tokens, s.hidden, s.inter, s.experts, s.top_k
+        self.inputs, self.touched, self.valid = [], [], []
+        for j in range(sets):
+            c = base if j == 0 else W.make_case(base.name, s, base.seed + 100000 * j, routing="uniform",
+                                                weight_seed=base.wseed)
+            self.inputs.append((D.to_dev(c.hidden_bits).view(torch.bfloat16), D.to_dev(c.topk_ids),
+                                D.to_dev(c.topk_weights)))
+            v = c.topk_ids[(c.topk_ids >= 0) & (c.topk_ids < self.E)]
+            self.touched.append(len(np.unique(v)))
+            self.valid.append(int(v.size))
+        self.acc = None
+        self.out = torch.empty((self.T, self.H), dtype=torch.bfloat16, device="cuda")
+
+
 def counter_traffic(workload, tag):
     """HBM bytes per FC1 launch from the committed rocprofv3 counter runs, or None
     when the kernel sources changed since those counters were taken."""
@@ -379,6 +404,24 @@ def main():
             pl.close()
             del pl, b
             torch.cuda.empty_cache()
+        # the pages' own expert shapes (hidden 3584, intermediate 3072, top-16, 224 of 896 experts)
+        case = W.k3_case(max(W.K3_DECODE_M))
+        t0 = time.time()
+        from workloads import device as D
+        w = D.upload_experts(case)
+        s = case.shape
+        pl = moe.Plan(moe.Config(s.hidden, s.inter, s.experts, s.top_k, max(W.K3_DECODE_M), moe.MOE_ACT_BF16), *w)
+        del w
+        torch.cuda.synchronize()
+        log(f"K3 shapes: plan built in {time.time() - t0:.1f}s")
+        for m in W.K3_DECODE_M:
+            b = K3Batches(pl, m, args.sets)
+            extra[f"k3_decode_m{m}"] = b.summary(b.run(max(20, args.steps), args.warmup))
+            log(f"K3 decode M={m}: {extra[f'k3_decode_m{m}']}")
+            del b
+        pl.close()
+        del pl
+        torch.cuda.empty_cache()
         extra["router_topk"] = router_timings()
         log(f"router: {extra['router_topk']}")
         line["extra"] = extra

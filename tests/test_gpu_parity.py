@@ -221,6 +221,30 @@ def test_forward_prefill(cid):
     say(f"  tokens {toks}: max_ulp={r['max_ulp']:.2f} max_rel_l2={r['max_rel_l2']:.2e}")
 
 
+# ------------------------------------------------------------------ the pages' K3 expert shapes (sampled tokens)
+@pytest.mark.parametrize("m,act", [(1, "bf16"), (16, "bf16"), (128, "bf16"), (512, "bf16"), (512, "mxfp8")])
+def test_forward_k3_shapes(m, act):
+    """Hidden 3584, intermediate 3072, top-16, 224 of 896 experts: decode buckets
+    on the streaming kernels, 512 tokens (8192 routes) on the prefill kernels."""
+    case = W.k3_case(m, act)
+    say(f"forward K3 shapes M={m} act={act}")
+    key = ("k3", act)
+    if key not in _plans:
+        _plans.clear()
+        torch.cuda.empty_cache()
+        say(f"  generating and repacking {case.shape.experts} K3 experts ({act})")
+        plan, w = G.make_plan(case, max_tokens=512)
+        del w
+        torch.cuda.synchronize()
+        _plans[key] = plan
+    out, acc = G.run_forward(_plans[key], case)
+    assert torch.isfinite(acc).all()
+    np.testing.assert_array_equal(G.bf16_bits(out), oracle.f32_to_bf16_rne(acc.cpu().numpy()))
+    toks = sampled_tokens(case, 3)
+    r = check_layer(case, out, acc, tokens=toks)
+    say(f"  tokens {toks}: max_ulp={r['max_ulp']:.2f} max_rel_l2={r['max_rel_l2']:.2e}")
+
+
 # ------------------------------------------------------------------ exact invariants (bitwise on the device)
 @pytest.fixture(scope="module")
 def mid():

@@ -40,6 +40,9 @@ __all__ = [
     "CONFIGS",
     "DECODE_M",
     "config_case",
+    "K3_SHAPE",
+    "K3_DECODE_M",
+    "k3_case",
     "make_case",
     "gen_hidden",
     "gen_routes",
@@ -231,6 +234,22 @@ def config_case(cid: int, m: Optional[int] = None, seed: Optional[int] = None) -
     if seed is None:
         seed = 1000 * cid + (int(m) if cid == 1 else 0)
     return make_case(name, shape, seed, weight_seed=1000 * cid, **c)
+
+
+# The pages' own expert shapes (Kimi K3, pegainfer PR #867, commit b49a9f04:
+# W13 N=6144 / K=3584, W2 N=3584 / K=3072; top-16; 224 or 896 routed experts,
+# batch buckets 1..128): one EP4 rank's share, 224 resident of 896, route ids
+# uniform over all 896 (ids >= 224 contribute an exact zero).  Not one of the
+# five configurations above; K3_PREFILL is a prefill-sized batch of the same
+# shapes (bf16 or MXFP8 activations).
+K3_SHAPE = LayerShape(None, 3584, 3072, 224, 896, 16)
+K3_DECODE_M = (1, 16, 128)
+
+
+def k3_case(m: int, act: str = "bf16") -> Case:
+    shape = dataclasses.replace(K3_SHAPE, tokens=int(m))
+    return make_case(f"k3_{act}_m{m}", shape, 6000 + int(m) + (500 if act == "mxfp8" else 0), routing="uniform",
+                     act=act, weight_seed=6000)
 
 
 def touched_experts(topk_ids: np.ndarray, experts: int) -> List[int]:
