@@ -23,8 +23,9 @@
 // requantises it in a separate pass).  FC2: fp32 y rows in route-row order.
 #include "moe_internal.h"
 
+// Weight loads with the non-temporal hint: bit 0 for FC1, bit 1 for FC2.
 #ifndef MOE_NT_LOADS
-#define MOE_NT_LOADS 0
+#define MOE_NT_LOADS 1
 #endif
 
 namespace moe {
@@ -76,13 +77,13 @@ __global__ __launch_bounds__(kWave * KSPLIT) void fc_dec(FcArgs a) {
 #pragma unroll
     for (int j = 0; j < NBW; ++j) {
       const uint4* wp = reinterpret_cast<const uint4*>(cbase + j * cstride + (size_t)kb * kTileBytes);
-#if MOE_NT_LOADS
-      typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
-      const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(wp));  // streamed once
-      w[j] = make_uint4(v[0], v[1], v[2], v[3]);
-#else
-      w[j] = *wp;
-#endif
+      if constexpr ((FC1 && (MOE_NT_LOADS & 1)) || (!FC1 && (MOE_NT_LOADS & 2))) {
+        typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+        const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(wp));  // streamed once
+        w[j] = make_uint4(v[0], v[1], v[2], v[3]);
+      } else {
+        w[j] = *wp;
+      }
       s[j] = *reinterpret_cast<const uint32_t*>(sbase + j * sstride + (size_t)(kb >> 2) * kScaleGroupBytes);
     }
     if constexpr (!MX) {

@@ -27,9 +27,14 @@
 // the plain (r & 7) swizzle leaves rows r and r + 8 colliding, about 1.6x
 // slower; unswizzled rows about 6x slower).
 //
-// Work order: the flat list (tile, column slice) is cut into eight contiguous
-// chunks, one per XCD (workgroups are dispatched round-robin over the XCDs),
-// so the tiles of one expert run together on one XCD and share its L2.
+// Work order: the flat list of (tile, column slice) items is cut into eight
+// contiguous chunks, one per XCD (workgroups are dispatched round-robin over
+// the XCDs).  Within it, items run in groups of kTileGroup consecutive tiles
+// as (group, slice, tile in group): the tiles of a group that belong to one
+// expert -- an expert with many rows has many consecutive tiles -- read the
+// same weight slice at the same time and share it in L2, while the slices of
+// one tile still fall within one XCD's concurrent workgroups and share the
+// tile's activation rows.
 #include "moe_internal.h"
 
 namespace moe {
@@ -44,6 +49,10 @@ constexpr int kBN = 256;                 // weight rows (output columns) per wor
 constexpr int kBlocks = kBN / kTileN;    // 16 repacked row blocks
 constexpr int kStageK = 64;              // K per pipeline stage (half a repacked tile)
 constexpr int kHalfTile = kTileBytes / 2;
+#ifndef MOE_PREFILL_TILE_GROUP
+#define MOE_PREFILL_TILE_GROUP 1
+#endif
+constexpr int kTileGroup = MOE_PREFILL_TILE_GROUP;   // tiles sharing a weight slice in flight
 
 template <int BM>
 struct Stage {
@@ -61,55 +70,69 @@ __device__ __forceinline__ int swz(int c, int r) { return c ^ (r & 7) ^ ((r >> 3
 // the compiler placed after the barrier still reads its result.
 #define MOE_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | ((((n) >> 4) & 3) << 14))
 
-// Per-lane global source pointers of one stage's global_load_lds: BM/32
-// activation chunks, two code chunks, two scale dwords.  Advance by stage:
+// Per-lane global source pointers of one stage's global_load_lds copies, for a
+// workgroup of W waves: BM/(8W) activation copies (eight rows each), 8/W code
+// copies (two half-tiles each) and 8/W scale copies.  Advance by stage:
 // activations +128 B, codes +512 B, scales per 128-K block (see scale_off).
-template <int BM>
+template <int BM, int W>
 struct StageSrc {
-  const uint8_t* a[BM / 32];
-  const uint8_t* b[2];
-  const uint8_t* s[2];
+  static constexpr int kA = BM / (8 * W), kB = 8 / W;
+  const uint8_t* a[kA];
+  const uint8_t* b[kB];
+  const uint8_t* s[kB];
 };
 
 __device__ __forceinline__ size_t scale_off(int st) {
   return (size_t)(st >> 3) * kScaleGroupBytes + (size_t)(st & 1) * 128;   // group of 4 blocks, half of the lanes
 }
 
-template <int BM>
-__device__ __forceinline__ void issue_stage(uint8_t* buf, const StageSrc<BM>& src, int st, int wave) {
-#pragma unroll
-  for (int j = 0; j < BM / 32; ++j)   // rows 8i..8i+7 of the stage, i = wave + 4j
+// Copy number c (0 .. kA + 2 kB - 1) of this wave's share of stage st.
+template <int BM, int W>
+__device__ __forceinline__ void issue_copy(uint8_t* buf, const StageSrc<BM, W>& src, int st, int wave, int c) {
+  using Src = StageSrc<BM, W>;
+  if (c < Src::kA) {                  // rows 8i..8i+7 of the stage, i = wave + W j
+    const int j = c;
     __builtin_amdgcn_global_load_lds((glob_void_t*)(src.a[j] + (size_t)st * (kStageK * 2)),
-                                     (lds_void_t*)(buf + (wave + 4 * j) * 1024), 16, 0, 0);
-#pragma unroll
-  for (int j = 0; j < 2; ++j)         // code half-tiles of row blocks 2i, 2i+1
+                                     (lds_void_t*)(buf + (wave + W * j) * 1024), 16, 0, 0);
+  } else if (c < Src::kA + Src::kB) {  // code half-tiles of row blocks 2i, 2i+1
+    const int j = c - Src::kA;
     __builtin_amdgcn_global_load_lds((glob_void_t*)(src.b[j] + (size_t)st * kHalfTile),
-                                     (lds_void_t*)(buf + Stage<BM>::kA + (wave + 4 * j) * 1024), 16, 0, 0);
-#pragma unroll
-  for (int j = 0; j < 2; ++j)         // their scale dwords
+                                     (lds_void_t*)(buf + Stage<BM>::kA + (wave + W * j) * 1024), 16, 0, 0);
+  } else {                             // their scale dwords
+    const int j = c - Src::kA - Src::kB;
     __builtin_amdgcn_global_load_lds((glob_void_t*)(src.s[j] + scale_off(st)),
-                                     (lds_void_t*)(buf + Stage<BM>::kA + Stage<BM>::kB + (wave + 4 * j) * 256), 4, 0,
+                                     (lds_void_t*)(buf + Stage<BM>::kA + Stage<BM>::kB + (wave + W * j) * 256), 4, 0,
                                      0);
+  }
 }
 
-// The K loop for a tile whose rows fill LIVE 32-row blocks (blocks past them
-// are padding and issue nothing).
-template <int BM, int LIVE>
-__device__ __forceinline__ void k_loop(uint8_t* smem, const StageSrc<BM>& src, int S, int wave, int lane,
-                                       f32x16_t (&acc)[BM / 32][2]) {
+template <int BM, int W>
+__device__ __forceinline__ void issue_stage(uint8_t* buf, const StageSrc<BM, W>& src, int st, int wave) {
+#pragma unroll
+  for (int c = 0; c < StageSrc<BM, W>::kA + 2 * StageSrc<BM, W>::kB; ++c) issue_copy<BM, W>(buf, src, st, wave, c);
+}
+
+// The K loop of one wave over its MI 32-row blocks, of which LIVE hold rows
+// (blocks past them are padding and issue nothing; a wave with LIVE = 0 still
+// copies its share of every stage and meets every barrier).  `wn` is the
+// wave's 64-column quarter, `row0` the first staged row of its blocks.
+template <int BM, int W, int MI, int LIVE>
+__device__ __forceinline__ void k_loop(uint8_t* smem, const StageSrc<BM, W>& src, int S, int wave, int wn, int row0,
+                                       int lane, f32x16_t (&acc)[MI][2]) {
   constexpr int NJ = 2;
-  constexpr int LOADS = BM / 32 + 4;
+  constexpr int LOADS = StageSrc<BM, W>::kA + 2 * StageSrc<BM, W>::kB;   // copies per stage per wave
+  constexpr int LA = LIVE > 0 ? LIVE : 1;
   const int n32 = lane & 31, h = lane >> 5;
   uint8_t* cur = smem;
   uint8_t* nxt = smem + Stage<BM>::kBytes;
   uint8_t* nxt2 = smem + 2 * Stage<BM>::kBytes;
-  issue_stage<BM>(cur, src, 0, wave);
-  if (S > 1) issue_stage<BM>(nxt, src, 1, wave);
+  issue_stage<BM, W>(cur, src, 0, wave);
+  if (S > 1) issue_stage<BM, W>(nxt, src, 1, wave);
   // this lane's reads inside a stage
   const int lp = (n32 & 15) + 16 * h;
-  const int boff = (wave * (2 * NJ) + (n32 >> 4)) * kHalfTile + lp * 16;  // + 2*nj*kHalfTile
-  const int soff = Stage<BM>::kA + Stage<BM>::kB + ((wave * (2 * NJ) + (n32 >> 4)) * 32 + lp) * 4;
-  const int aoff = n32 * (kStageK * 2);
+  const int boff = (wn * (2 * NJ) + (n32 >> 4)) * kHalfTile + lp * 16;  // + 2*nj*kHalfTile
+  const int soff = Stage<BM>::kA + Stage<BM>::kB + ((wn * (2 * NJ) + (n32 >> 4)) * 32 + lp) * 4;
+  const int aoff = (row0 + n32) * (kStageK * 2);   // row0 is a multiple of 32: the swizzle sees n32
   for (int st = 0; st < S; ++st) {
     if (st + 1 < S) MOE_WAIT_VMCNT(LOADS);   // this wave's loads of stage st have landed
     else MOE_WAIT_VMCNT(0);
@@ -119,43 +142,55 @@ __device__ __forceinline__ void k_loop(uint8_t* smem, const StageSrc<BM>& src, i
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    if (st + 2 < S) issue_stage<BM>(nxt2, src, st + 2, wave);
-    const int sh = ((st >> 1) & 3) * 8;
-    u32x4_t bc[NJ];
-    float bs[NJ];
+    // stage st+2's copies go out a quarter per k-step, between the MFMA
+    // batches: issued all at once after the barrier, every wave's copies queue
+    // on the CU's texture path together and hold back its first MFMAs
+    const bool refill = st + 2 < S;
+    if constexpr (LIVE == 0) {
+      if (refill) issue_stage<BM, W>(nxt2, src, st + 2, wave);
+    } else {
+      const int sh = ((st >> 1) & 3) * 8;
+      u32x4_t bc[NJ];
+      float bs[NJ];
 #pragma unroll
-    for (int nj = 0; nj < NJ; ++nj) {
-      bc[nj] = *reinterpret_cast<const u32x4_t*>(cur + Stage<BM>::kA + boff + 2 * nj * kHalfTile);
-      bs[nj] = e8m0_to_f32((*reinterpret_cast<const uint32_t*>(cur + soff + 2 * nj * 32 * 4) >> sh) & 0xFFu);
-    }
-    // Step s+1's activation fragments are read while step s multiplies: the
-    // scheduling barriers pin each batch of LDS reads ahead of the MFMAs that
-    // follow, so a wave waits on LDS latency once per stage, not once per step.
-    const uint8_t* arow = cur + aoff;
-    bf16x8_t Ac[LIVE], An[LIVE];
-#pragma unroll
-    for (int mi = 0; mi < LIVE; ++mi)
-      Ac[mi] = *reinterpret_cast<const bf16x8_t*>(arow + mi * 32 * (kStageK * 2) + swz(4 * h, n32) * 16);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      if (s < 3) {
-#pragma unroll
-        for (int mi = 0; mi < LIVE; ++mi)
-          An[mi] = *reinterpret_cast<const bf16x8_t*>(arow + mi * 32 * (kStageK * 2) + swz(4 * h + s + 1, n32) * 16);
-        __builtin_amdgcn_sched_barrier(0);
+      for (int nj = 0; nj < NJ; ++nj) {
+        bc[nj] = *reinterpret_cast<const u32x4_t*>(cur + Stage<BM>::kA + boff + 2 * nj * kHalfTile);
+        bs[nj] = e8m0_to_f32((*reinterpret_cast<const uint32_t*>(cur + soff + 2 * nj * 32 * 4) >> sh) & 0xFFu);
       }
-      bf16x8_t B[NJ];
-#pragma unroll
-      for (int nj = 0; nj < NJ; ++nj) B[nj] = dequant8(bc[nj][s], bs[nj]);
+      // Step s+1's activation fragments are read while step s multiplies: the
+      // scheduling barriers pin each batch of LDS reads ahead of the MFMAs that
+      // follow, so a wave waits on LDS latency once per stage, not once per step.
+      const uint8_t* arow = cur + aoff;
+      bf16x8_t Ac[LA], An[LA];
 #pragma unroll
       for (int mi = 0; mi < LIVE; ++mi)
+        Ac[mi] = *reinterpret_cast<const bf16x8_t*>(arow + mi * 32 * (kStageK * 2) + swz(4 * h, n32) * 16);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int nj = 0; nj < NJ; ++nj)
-          acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Ac[mi], B[nj], acc[mi][nj], 0, 0, 0);
-      if (s < 3) {
+      for (int s = 0; s < 4; ++s) {
+        if (refill) {
 #pragma unroll
-        for (int mi = 0; mi < LIVE; ++mi) Ac[mi] = An[mi];
+          for (int c = s * LOADS / 4; c < (s + 1) * LOADS / 4; ++c) issue_copy<BM, W>(nxt2, src, st + 2, wave, c);
+        }
+        if (s < 3) {
+#pragma unroll
+          for (int mi = 0; mi < LIVE; ++mi)
+            An[mi] =
+                *reinterpret_cast<const bf16x8_t*>(arow + mi * 32 * (kStageK * 2) + swz(4 * h + s + 1, n32) * 16);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        bf16x8_t B[NJ];
+#pragma unroll
+        for (int nj = 0; nj < NJ; ++nj) B[nj] = dequant8(bc[nj][s], bs[nj]);
+#pragma unroll
+        for (int mi = 0; mi < LIVE; ++mi)
+#pragma unroll
+          for (int nj = 0; nj < NJ; ++nj)
+            acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Ac[mi], B[nj], acc[mi][nj], 0, 0, 0);
+        if (s < 3) {
+#pragma unroll
+          for (int mi = 0; mi < LIVE; ++mi) Ac[mi] = An[mi];
+        }
       }
     }
     uint8_t* t = cur;
@@ -165,43 +200,61 @@ __device__ __forceinline__ void k_loop(uint8_t* smem, const StageSrc<BM>& src, i
   }
 }
 
-template <bool FC1, int BM>
-__global__ __launch_bounds__(256, 2) void fc_pre(FcArgs a, int slices) {
-  constexpr int MI = BM / 32;                // 32-row MFMA blocks per wave (all rows of the tile)
+// W = 4: each wave owns all BM rows x one 64-column quarter (every weight
+// fragment dequantised once per workgroup; two workgroups per CU).  W = 8: the
+// quarters are split again into two 64-row halves, so a wave holds half the
+// accumulators and four waves share a SIMD (two workgroups per CU) to hide
+// each other's LDS and barrier waits; both halves dequantise the quarter's
+// fragments.
+template <bool FC1, int BM, int W>
+__global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(W / 2, W / 2))) void fc_pre(FcArgs a,
+                                                                                                 int slices) {
+  constexpr int RH = W / 4;                  // row groups
+  constexpr int MI = BM / 32 / RH;           // 32-row MFMA blocks per wave
   constexpr int NJ = 2;                      // 32-column MFMA blocks per wave (its 64-column quarter)
   __shared__ __align__(1024) uint8_t smem[3 * Stage<BM>::kBytes];
 
   const int ntiles = *a.tile_count;
-  const int total = ntiles * slices;
+  const int total = (ntiles + kTileGroup - 1) / kTileGroup * kTileGroup * slices;   // whole groups
   const int xcd = blockIdx.x & 7, qq = blockIdx.x >> 3;
   const int chunk = (total + 7) >> 3;
   const int w = xcd * chunk + qq;
   if (qq >= chunk || w >= total) return;
-  const int tile = w / slices, slice = w - tile * slices;
+  // items in groups of kTileGroup consecutive tiles: (group, slice, tile in group)
+  const int per_group = kTileGroup * slices;
+  const int grp = w / per_group, rem = w - grp * per_group;
+  const int slice = rem / kTileGroup, tile = grp * kTileGroup + (rem - slice * kTileGroup);
+  if (tile >= ntiles) return;
   const int2 td = a.tiles[tile];
   const int e = td.x, row0 = td.y;
   const int rows = min(BM, a.offsets[e + 1] - row0);
   const MatLayout M = a.mat;
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int wn = wave;                       // the four waves split the 256 columns
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int wn = wave & 3;                   // 64-column quarter
+  const int wr = wave >> 2;                  // row group
+  const int r0 = wr * MI * 32;               // first row of this wave's blocks
   const int nb0 = slice * kBlocks;
-  const int live = (rows + 31) >> 5;         // 32-row blocks holding at least one row
+  // this wave's blocks holding a row (W = 4: all rows, 1..4; the clamped form
+  // there would make the compiler spill the accumulators)
+  const int live = W == 4 ? (rows + 31) >> 5 : min(MI, max(0, (rows - r0 + 31) >> 5));
 
-  StageSrc<BM> src;
-  // activation chunks this lane copies: instruction i = wave + 4j writes rows
+  using Src = StageSrc<BM, W>;
+  Src src;
+  // activation chunks this lane copies: copy i = wave + W j writes rows
   // 8i..8i+7 (128 bytes each); lane L fills row 8i + L/8 at position L%8 with
   // the K chunk c that the swizzle places there.
 #pragma unroll
-  for (int j = 0; j < BM / 32; ++j) {
-    const int r = 8 * (wave + 4 * j) + (lane >> 3);
+  for (int j = 0; j < Src::kA; ++j) {
+    const int r = 8 * (wave + W * j) + (lane >> 3);
     const int rr = min(r, rows - 1);
     const int ar = FC1 ? a.perm[row0 + rr] / a.top_k : row0 + rr;
     src.a[j] = static_cast<const uint8_t*>(a.a) + (size_t)ar * a.lda * 2 + swz(lane & 7, r) * 16;
   }
-  // codes / scales this lane copies: row block 2(wave + 4j) + lane/32, chunk or dword lane%32
+  // codes / scales this lane copies: row block 2(wave + W j) + lane/32, chunk or dword lane%32
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int blk = nb0 + 2 * (wave + 4 * j) + (lane >> 5);
+  for (int j = 0; j < Src::kB; ++j) {
+    const int blk = nb0 + 2 * (wave + W * j) + (lane >> 5);
     src.b[j] = a.codes + ((size_t)e * M.nb + blk) * M.kb * kTileBytes + (lane & 31) * 16;
     src.s[j] = a.scales + ((size_t)e * M.nb + blk) * M.kb4 * kScaleGroupBytes + (lane & 31) * 4;
   }
@@ -215,16 +268,21 @@ __global__ __launch_bounds__(256, 2) void fc_pre(FcArgs a, int slices) {
       for (int i = 0; i < 16; ++i) acc[mi][nj][i] = 0.f;
 
   const int S = 2 * M.kb;    // stages
-  if constexpr (MI == 4) {
+  if constexpr (MI == 4) {   // W = 4: every wave holds row 0, so live >= 1
     switch (live) {
-      case 1: k_loop<BM, 1>(smem, src, S, wave, lane, acc); break;
-      case 2: k_loop<BM, 2>(smem, src, S, wave, lane, acc); break;
-      case 3: k_loop<BM, 3>(smem, src, S, wave, lane, acc); break;
-      default: k_loop<BM, 4>(smem, src, S, wave, lane, acc); break;
+      case 1: k_loop<BM, W, MI, 1>(smem, src, S, wave, wn, r0, lane, acc); break;
+      case 2: k_loop<BM, W, MI, 2>(smem, src, S, wave, wn, r0, lane, acc); break;
+      case 3: k_loop<BM, W, MI, 3>(smem, src, S, wave, wn, r0, lane, acc); break;
+      default: k_loop<BM, W, MI, 4>(smem, src, S, wave, wn, r0, lane, acc); break;
     }
   } else {
-    if (live == 1) k_loop<BM, 1>(smem, src, S, wave, lane, acc);
-    else k_loop<BM, 2>(smem, src, S, wave, lane, acc);
+    switch (live) {
+      case 0:
+        if constexpr (W > 4) k_loop<BM, W, MI, 0>(smem, src, S, wave, wn, r0, lane, acc);
+        break;
+      case 1: k_loop<BM, W, MI, 1>(smem, src, S, wave, wn, r0, lane, acc); break;
+      default: k_loop<BM, W, MI, 2>(smem, src, S, wave, wn, r0, lane, acc); break;
+    }
   }
   const int n32 = lane & 31, h = lane >> 5;
 
@@ -236,7 +294,7 @@ __global__ __launch_bounds__(256, 2) void fc_pre(FcArgs a, int slices) {
     for (int nj = 0; nj < NJ; ++nj) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int r = mi * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
+        const int r = r0 + mi * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
         const float v = acc[mi][nj][i];
         if constexpr (FC1) {
           // columns 0..15 of the block pair are gate j, 16..31 up j (interleaved row blocks)
@@ -256,12 +314,17 @@ __global__ __launch_bounds__(256, 2) void fc_pre(FcArgs a, int slices) {
   }
 }
 
+#ifndef MOE_PREFILL_WAVES
+#define MOE_PREFILL_WAVES 4
+#endif
+
 template <bool FC1, int BM>
 hipError_t launch_pre(const FcArgs& a, int tiles_max, hipStream_t stream) {
+  constexpr int W = BM == 128 ? MOE_PREFILL_WAVES : 4;
   const int slices = a.mat.nb / kBlocks;
-  const long long items = (long long)tiles_max * slices;
+  const long long items = (long long)((tiles_max + kTileGroup - 1) / kTileGroup * kTileGroup) * slices;
   const long long grid = (items + 7) / 8 * 8;
-  hipLaunchKernelGGL((fc_pre<FC1, BM>), dim3((unsigned)grid), dim3(256), 0, stream, a, slices);
+  hipLaunchKernelGGL((fc_pre<FC1, BM, W>), dim3((unsigned)grid), dim3(W * kWave), 0, stream, a, slices);
   return hipGetLastError();
 }
 
