@@ -148,7 +148,31 @@ SMALL = [
     ("odd_hidden", lambda: W.make_case("odd_hidden", W.LayerShape(100, 384, 256, 3, 3, 2), 37, routing="uniform")),
     ("odd_hidden_mx", lambda: W.make_case("odd_hidden_mx", W.LayerShape(100, 384, 256, 3, 3, 2), 38,
                                           routing="uniform", act="mxfp8")),
+    # one expert, top-1 (a dense gated MLP per token): every row in one expert, three 128-row tiles
+    ("single_expert", lambda: W.make_case("single_expert", W.LayerShape(300, 256, 128, 1, 1, 1), 39)),
+    # the largest top-k the library takes
+    ("top32", lambda: W.make_case("top32", W.LayerShape(5, 256, 128, 40, 48, 32), 40, invalid_frac=0.05)),
+    # K at the largest hidden / intermediate a plan takes, on the streaming (few tokens) and the
+    # prefill (>= 16 routes per expert) kernels, bf16 and MXFP8
+    ("max_hidden", lambda: W.make_case("max_hidden", W.LayerShape(6, 16384, 256, 2, 2, 1), 41)),
+    ("max_hidden_pre", lambda: W.make_case("max_hidden_pre", W.LayerShape(64, 16384, 256, 2, 2, 1), 42)),
+    ("max_hidden_pre_mx", lambda: W.make_case("max_hidden_pre_mx", W.LayerShape(64, 16384, 256, 2, 2, 1), 43,
+                                              act="mxfp8")),
+    ("max_inter", lambda: W.make_case("max_inter", W.LayerShape(6, 256, 16384, 2, 2, 1), 44)),
+    ("max_inter_pre_mx", lambda: W.make_case("max_inter_pre_mx", W.LayerShape(64, 256, 16384, 2, 2, 1), 45,
+                                             act="mxfp8")),
 ]
+
+
+def test_forward_duplicate_expert_ids():
+    """A token may name one expert in several slots; each route counts."""
+    shape = W.LayerShape(2, 256, 128, 2, 2, 3)
+    base = W.make_case("dups", shape, 46)
+    ids = np.array([[1, 1, 1], [0, 1, 0]], np.int32)
+    case = W.Case(base.name, shape, base.seed, base.hidden_bits, ids, base.topk_weights, 120, 130)
+    plan, _ = G.make_plan(case)
+    out, acc = G.run_forward(plan, case)
+    check_layer(case, out, acc, ew=case.experts())
 
 
 @pytest.mark.parametrize("name,make", SMALL, ids=[s[0] for s in SMALL])
