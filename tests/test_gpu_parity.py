@@ -82,6 +82,8 @@ def test_route_bitexact(cid, m):
     (np.array([[1, 1, 1], [1, 0, 1]], np.int32), 2),                   # duplicates
     (np.array([[7, 3, 2, 9]], np.int32), 8),                           # one token, one non-resident
     (np.random.default_rng(3).integers(-2, 40, (700, 3)).astype(np.int32), 33),   # 2100 routes: chunked path
+    (np.random.default_rng(4).integers(-2, 1030, (32, 8)).astype(np.int32), 1024),  # 256 routes, E = 1024: one wave
+    (np.random.default_rng(5).integers(-1, 1000, (257, 1)).astype(np.int32), 1000),  # 257: one workgroup
 ])
 def test_route_edge_cases(ids, E):
     say(f"route edge case T={ids.shape[0]} k={ids.shape[1]} E={E}")
