@@ -10,7 +10,19 @@
 // registers with the gfx950 scaled converter (value * 2^(scale-127), exact in
 // bf16): every converted fragment feeds BM/32 MFMAs, and a code byte crosses
 // LDS once instead of as two bf16 bytes per weight.  32-row blocks that lie
-// wholly past the tile's rows (Zipf-routed experts leave many) issue no MFMA.
+// wholly past the tile's rows (Zipf-routed experts leave many) issue no MFMA
+// and their activation rows are not copied.
+//
+// Step order inside a stage: the first MFMA of a step (its operands were read
+// a step earlier), then the step's share of the next copies, then the next
+// step's LDS reads, then the other MFMAs.  The compiler stops counting LDS
+// reads precisely once an LDS-DMA copy is issued behind them and waits for
+// lgkmcnt(0) at their first use; in this order that wait only ever covers
+// reads that are a full step old.
+//
+// A build with MOE_PREFILL_WN=8 runs eight waves over 512 columns (one
+// workgroup per CU, a third less copying per MFMA); measured slower than two
+// four-wave workgroups per CU, so not the default.
 //
 // MFMA K order: in the stage covering K [64q, 64q+64) of a 128-K column block
 // (q = 0, 1), step s (16 K) of lane l (column n = l%32, half h = l/32)
@@ -45,8 +57,6 @@ typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void glob_void_t;
 
-constexpr int kBN = 256;                 // weight rows (output columns) per workgroup
-constexpr int kBlocks = kBN / kTileN;    // 16 repacked row blocks
 constexpr int kStageK = 64;              // K per pipeline stage (half a repacked tile)
 constexpr int kHalfTile = kTileBytes / 2;
 #ifndef MOE_PREFILL_TILE_GROUP
@@ -54,12 +64,31 @@ constexpr int kHalfTile = kTileBytes / 2;
 #endif
 constexpr int kTileGroup = MOE_PREFILL_TILE_GROUP;   // tiles sharing a weight slice in flight
 
-template <int BM>
-struct Stage {
-  static constexpr int kA = BM * kStageK * 2;        // activation rows
-  static constexpr int kB = kBlocks * kHalfTile;     // code half-tiles
-  static constexpr int kS = kBlocks * 32 * 4;        // scale dwords of the half
+// Workgroup shape: W waves side by side over the columns (64 each, four
+// 16-column row blocks), every wave over all BM rows.  One pipeline stage
+// holds the BM activation rows of 64 K (bf16), the code half-tiles of the
+// workgroup's row blocks and their scale dwords; each wave copies an equal
+// share of it.
+template <int BM, int W_>
+struct Cfg {
+  static constexpr int W = W_;
+  static constexpr int kBlocks = 4 * W;                  // repacked row blocks per workgroup
+  static constexpr int kA = BM * kStageK * 2;            // activation rows
+  static constexpr int kB = kBlocks * kHalfTile;         // code half-tiles
+  static constexpr int kS = kBlocks * 32 * 4;            // scale dwords of the half
   static constexpr int kBytes = kA + kB + kS;
+  static constexpr int nA = BM / 8 / W;                  // 1 KB copies of eight activation rows
+  static constexpr int nB = kBlocks / 2 / W;             // 1 KB copies of two code half-tiles
+  static constexpr int nS = nB;                          // 256 B copies of their scale dwords
+  static constexpr int MI = BM / 32;                     // 32-row MFMA blocks per wave
+  // activation copies per wave when only the first `live` 32-row blocks hold rows
+  static constexpr int nA_live(int live) { return (4 * live + W - 1) / W < nA ? (4 * live + W - 1) / W : nA; }
+  static constexpr int copies(int live) { return nA_live(live) + nB + nS; }
+  // workgroups per CU that the three stage buffers allow (at most two), and
+  // the waves per SIMD that gives
+  static constexpr int kPerCU = 3 * kBytes * 2 <= 160 * 1024 ? 2 : 1;
+  static constexpr int kWavesPerSimd = kPerCU * W / 4;
+  static_assert(nA * 8 * W == BM && nB * 2 * W == kBlocks, "copies split evenly over the waves");
 };
 
 // LDS position of K chunk c (0..7) in staged activation row r.
@@ -70,69 +99,66 @@ __device__ __forceinline__ int swz(int c, int r) { return c ^ (r & 7) ^ ((r >> 3
 // the compiler placed after the barrier still reads its result.
 #define MOE_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | ((((n) >> 4) & 3) << 14))
 
-// Per-lane global source pointers of one stage's global_load_lds copies, for a
-// workgroup of W waves: BM/(8W) activation copies (eight rows each), 8/W code
-// copies (two half-tiles each) and 8/W scale copies.  Advance by stage:
-// activations +128 B, codes +512 B, scales per 128-K block (see scale_off).
-template <int BM, int W>
+// Per-lane global source pointers of one wave's copies: activation rows,
+// code half-tiles, scale dwords.  Advance by stage: activations +128 B, codes
+// +512 B, scales per 128-K block (see scale_off).
+template <class C>
 struct StageSrc {
-  static constexpr int kA = BM / (8 * W), kB = 8 / W;
-  const uint8_t* a[kA];
-  const uint8_t* b[kB];
-  const uint8_t* s[kB];
+  const uint8_t* a[C::nA];
+  const uint8_t* b[C::nB];
+  const uint8_t* s[C::nS];
 };
 
 __device__ __forceinline__ size_t scale_off(int st) {
   return (size_t)(st >> 3) * kScaleGroupBytes + (size_t)(st & 1) * 128;   // group of 4 blocks, half of the lanes
 }
 
-// Copy number c (0 .. kA + 2 kB - 1) of this wave's share of stage st.
-template <int BM, int W>
-__device__ __forceinline__ void issue_copy(uint8_t* buf, const StageSrc<BM, W>& src, int st, int wave, int c) {
-  using Src = StageSrc<BM, W>;
-  if (c < Src::kA) {                  // rows 8i..8i+7 of the stage, i = wave + W j
+// Copy number c (0 .. copies(LIVE)-1) of this wave's share of stage st.
+template <class C, int LIVE>
+__device__ __forceinline__ void issue_copy(uint8_t* buf, const StageSrc<C>& src, int st, int wave, int c) {
+  constexpr int W = C::W;
+  constexpr int NA = C::nA_live(LIVE);
+  if (c < NA) {                      // rows 8i..8i+7 of the stage, i = wave + W j
     const int j = c;
     __builtin_amdgcn_global_load_lds((glob_void_t*)(src.a[j] + (size_t)st * (kStageK * 2)),
                                      (lds_void_t*)(buf + (wave + W * j) * 1024), 16, 0, 0);
-  } else if (c < Src::kA + Src::kB) {  // code half-tiles of row blocks 2i, 2i+1
-    const int j = c - Src::kA;
+  } else if (c < NA + C::nB) {        // code half-tiles of row blocks 2i, 2i+1
+    const int j = c - NA;
     __builtin_amdgcn_global_load_lds((glob_void_t*)(src.b[j] + (size_t)st * kHalfTile),
-                                     (lds_void_t*)(buf + Stage<BM>::kA + (wave + W * j) * 1024), 16, 0, 0);
-  } else {                             // their scale dwords
-    const int j = c - Src::kA - Src::kB;
+                                     (lds_void_t*)(buf + C::kA + (wave + W * j) * 1024), 16, 0, 0);
+  } else {                            // their scale dwords
+    const int j = c - NA - C::nB;
     __builtin_amdgcn_global_load_lds((glob_void_t*)(src.s[j] + scale_off(st)),
-                                     (lds_void_t*)(buf + Stage<BM>::kA + Stage<BM>::kB + (wave + W * j) * 256), 4, 0,
-                                     0);
+                                     (lds_void_t*)(buf + C::kA + C::kB + (wave + W * j) * 256), 4, 0, 0);
   }
 }
 
-template <int BM, int W>
-__device__ __forceinline__ void issue_stage(uint8_t* buf, const StageSrc<BM, W>& src, int st, int wave) {
+template <class C, int LIVE>
+__device__ __forceinline__ void issue_stage(uint8_t* buf, const StageSrc<C>& src, int st, int wave) {
 #pragma unroll
-  for (int c = 0; c < StageSrc<BM, W>::kA + 2 * StageSrc<BM, W>::kB; ++c) issue_copy<BM, W>(buf, src, st, wave, c);
+  for (int c = 0; c < C::copies(LIVE); ++c) issue_copy<C, LIVE>(buf, src, st, wave, c);
 }
 
 // The K loop of one wave over its MI 32-row blocks, of which LIVE hold rows
-// (blocks past them are padding and issue nothing; a wave with LIVE = 0 still
-// copies its share of every stage and meets every barrier).  `wn` is the
-// wave's 64-column quarter, `row0` the first staged row of its blocks.
-template <int BM, int W, int MI, int LIVE>
-__device__ __forceinline__ void k_loop(uint8_t* smem, const StageSrc<BM, W>& src, int S, int wave, int wn, int row0,
-                                       int lane, f32x16_t (&acc)[MI][2]) {
+// (blocks past them are padding: their activations are neither copied nor
+// multiplied).  `wn` is the wave's 64-column group.
+template <class C, int LIVE>
+__device__ __forceinline__ void k_loop(uint8_t* smem, const StageSrc<C>& src, int S, int wave, int lane,
+                                       f32x16_t (&acc)[C::MI][2]) {
   constexpr int NJ = 2;
-  constexpr int LOADS = StageSrc<BM, W>::kA + 2 * StageSrc<BM, W>::kB;   // copies per stage per wave
-  constexpr int LA = LIVE > 0 ? LIVE : 1;
+  constexpr int LOADS = C::copies(LIVE);
+  const int wn = wave;
   const int n32 = lane & 31, h = lane >> 5;
   uint8_t* cur = smem;
-  uint8_t* nxt = smem + Stage<BM>::kBytes;
-  uint8_t* nxt2 = smem + 2 * Stage<BM>::kBytes;
-  issue_stage<BM, W>(cur, src, 0, wave);
-  if (S > 1) issue_stage<BM, W>(nxt, src, 1, wave);
+  uint8_t* nxt = smem + C::kBytes;
+  uint8_t* nxt2 = smem + 2 * C::kBytes;
+  issue_stage<C, LIVE>(cur, src, 0, wave);
+  if (S > 1) issue_stage<C, LIVE>(nxt, src, 1, wave);
   // this lane's reads inside a stage
   const int lp = (n32 & 15) + 16 * h;
   const int boff = (wn * (2 * NJ) + (n32 >> 4)) * kHalfTile + lp * 16;  // + 2*nj*kHalfTile
-  const int soff = Stage<BM>::kA + Stage<BM>::kB + ((wn * (2 * NJ) + (n32 >> 4)) * 32 + lp) * 4;
-  const int aoff = (row0 + n32) * (kStageK * 2);   // row0 is a multiple of 32: the swizzle sees n32
+  const int soff = C::kA + C::kB + ((wn * (2 * NJ) + (n32 >> 4)) * 32 + lp) * 4;
+  const int aoff = n32 * (kStageK * 2);
   for (int st = 0; st < S; ++st) {
     if (st + 1 < S) MOE_WAIT_VMCNT(LOADS);   // this wave's loads of stage st have landed
     else MOE_WAIT_VMCNT(0);
@@ -146,51 +172,56 @@ __device__ __forceinline__ void k_loop(uint8_t* smem, const StageSrc<BM, W>& src
     // batches: issued all at once after the barrier, every wave's copies queue
     // on the CU's texture path together and hold back its first MFMAs
     const bool refill = st + 2 < S;
-    if constexpr (LIVE == 0) {
-      if (refill) issue_stage<BM, W>(nxt2, src, st + 2, wave);
-    } else {
-      const int sh = ((st >> 1) & 3) * 8;
-      u32x4_t bc[NJ];
-      float bs[NJ];
+    const int sh = ((st >> 1) & 3) * 8;
+    u32x4_t bc[NJ];
+    float bs[NJ];
 #pragma unroll
-      for (int nj = 0; nj < NJ; ++nj) {
-        bc[nj] = *reinterpret_cast<const u32x4_t*>(cur + Stage<BM>::kA + boff + 2 * nj * kHalfTile);
-        bs[nj] = e8m0_to_f32((*reinterpret_cast<const uint32_t*>(cur + soff + 2 * nj * 32 * 4) >> sh) & 0xFFu);
+    for (int nj = 0; nj < NJ; ++nj) {
+      bc[nj] = *reinterpret_cast<const u32x4_t*>(cur + C::kA + boff + 2 * nj * kHalfTile);
+      bs[nj] = e8m0_to_f32((*reinterpret_cast<const uint32_t*>(cur + soff + 2 * nj * 32 * 4) >> sh) & 0xFFu);
+    }
+    // Step s+1's activation fragments are read while step s multiplies.  Per
+    // step: the dequantised weights and the first MFMA (the compiler waits
+    // there for this step's fragments, read a step earlier), then this step's
+    // share of the copies, in a block of its own, then the next step's reads
+    // and the other MFMAs.  A copy issued while an LDS read is outstanding
+    // makes the compiler wait with lgkmcnt(0) at that read's first use -- with
+    // the next step's reads already issued, that wait would cover them too.
+    const uint8_t* arow = cur + aoff;
+    bf16x8_t Ac[LIVE], An[LIVE];
+#pragma unroll
+    for (int mi = 0; mi < LIVE; ++mi)
+      Ac[mi] = *reinterpret_cast<const bf16x8_t*>(arow + mi * 32 * (kStageK * 2) + swz(4 * h, n32) * 16);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      bf16x8_t B[NJ];
+#pragma unroll
+      for (int nj = 0; nj < NJ; ++nj) B[nj] = dequant8(bc[nj][s], bs[nj]);
+      acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Ac[0], B[0], acc[0][0], 0, 0, 0);
+      if (refill) {
+#pragma unroll
+        for (int c = s * LOADS / 4; c < (s + 1) * LOADS / 4; ++c)
+          issue_copy<C, LIVE>(nxt2, src, st + 2, wave, c);
       }
-      // Step s+1's activation fragments are read while step s multiplies: the
-      // scheduling barriers pin each batch of LDS reads ahead of the MFMAs that
-      // follow, so a wave waits on LDS latency once per stage, not once per step.
-      const uint8_t* arow = cur + aoff;
-      bf16x8_t Ac[LA], An[LA];
-#pragma unroll
-      for (int mi = 0; mi < LIVE; ++mi)
-        Ac[mi] = *reinterpret_cast<const bf16x8_t*>(arow + mi * 32 * (kStageK * 2) + swz(4 * h, n32) * 16);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        if (refill) {
-#pragma unroll
-          for (int c = s * LOADS / 4; c < (s + 1) * LOADS / 4; ++c) issue_copy<BM, W>(nxt2, src, st + 2, wave, c);
-        }
-        if (s < 3) {
-#pragma unroll
-          for (int mi = 0; mi < LIVE; ++mi)
-            An[mi] =
-                *reinterpret_cast<const bf16x8_t*>(arow + mi * 32 * (kStageK * 2) + swz(4 * h + s + 1, n32) * 16);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        bf16x8_t B[NJ];
-#pragma unroll
-        for (int nj = 0; nj < NJ; ++nj) B[nj] = dequant8(bc[nj][s], bs[nj]);
+      if (s < 3) {
 #pragma unroll
         for (int mi = 0; mi < LIVE; ++mi)
+          An[mi] =
+              *reinterpret_cast<const bf16x8_t*>(arow + mi * 32 * (kStageK * 2) + swz(4 * h + s + 1, n32) * 16);
+      }
 #pragma unroll
-          for (int nj = 0; nj < NJ; ++nj)
+      for (int mi = 0; mi < LIVE; ++mi)
+#pragma unroll
+        for (int nj = 0; nj < NJ; ++nj)
+          if (mi + nj > 0)
             acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Ac[mi], B[nj], acc[mi][nj], 0, 0, 0);
-        if (s < 3) {
+      // the reads first (left to itself the compiler puts them behind the MFMAs)
+      if (s < 3) __builtin_amdgcn_sched_group_barrier(0x100, LIVE, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, NJ * LIVE - 1, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      if (s < 3) {
 #pragma unroll
-          for (int mi = 0; mi < LIVE; ++mi) Ac[mi] = An[mi];
-        }
+        for (int mi = 0; mi < LIVE; ++mi) Ac[mi] = An[mi];
       }
     }
     uint8_t* t = cur;
@@ -200,19 +231,19 @@ __device__ __forceinline__ void k_loop(uint8_t* smem, const StageSrc<BM, W>& src
   }
 }
 
-// W = 4: each wave owns all BM rows x one 64-column quarter (every weight
-// fragment dequantised once per workgroup; two workgroups per CU).  W = 8: the
-// quarters are split again into two 64-row halves, so a wave holds half the
-// accumulators and four waves share a SIMD (two workgroups per CU) to hide
-// each other's LDS and barrier waits; both halves dequantise the quarter's
-// fragments.
+// W waves side by side: each owns all BM rows x one 64-column group, so every
+// weight fragment is dequantised once per workgroup.  W = 4: two workgroups
+// per CU.  W = 8: 512 columns per workgroup, one per CU -- each staged
+// activation row serves twice the columns, but all eight waves meet at every
+// stage barrier with no second workgroup to fill the gaps.
 template <bool FC1, int BM, int W>
-__global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(W / 2, W / 2))) void fc_pre(FcArgs a,
-                                                                                                 int slices) {
-  constexpr int RH = W / 4;                  // row groups
-  constexpr int MI = BM / 32 / RH;           // 32-row MFMA blocks per wave
-  constexpr int NJ = 2;                      // 32-column MFMA blocks per wave (its 64-column quarter)
-  __shared__ __align__(1024) uint8_t smem[3 * Stage<BM>::kBytes];
+__global__ __launch_bounds__(W * kWave)
+__attribute__((amdgpu_waves_per_eu(Cfg<BM, W>::kWavesPerSimd, Cfg<BM, W>::kWavesPerSimd)))
+void fc_pre(FcArgs a, int slices) {
+  using C = Cfg<BM, W>;
+  constexpr int MI = C::MI;
+  constexpr int NJ = 2;                      // 32-column MFMA blocks per wave (its 64 columns)
+  __shared__ __align__(1024) uint8_t smem[3 * C::kBytes];
 
   const int ntiles = *a.tile_count;
   const int total = (ntiles + kTileGroup - 1) / kTileGroup * kTileGroup * slices;   // whole groups
@@ -231,21 +262,15 @@ __global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(W / 2
   const MatLayout M = a.mat;
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
-  const int wn = wave & 3;                   // 64-column quarter
-  const int wr = wave >> 2;                  // row group
-  const int r0 = wr * MI * 32;               // first row of this wave's blocks
-  const int nb0 = slice * kBlocks;
-  // this wave's blocks holding a row (W = 4: all rows, 1..4; the clamped form
-  // there would make the compiler spill the accumulators)
-  const int live = W == 4 ? (rows + 31) >> 5 : min(MI, max(0, (rows - r0 + 31) >> 5));
+  const int nb0 = slice * C::kBlocks;
+  const int live = (rows + 31) >> 5;         // 32-row blocks holding a row, 1..MI
 
-  using Src = StageSrc<BM, W>;
-  Src src;
+  StageSrc<C> src;
   // activation chunks this lane copies: copy i = wave + W j writes rows
   // 8i..8i+7 (128 bytes each); lane L fills row 8i + L/8 at position L%8 with
   // the K chunk c that the swizzle places there.
 #pragma unroll
-  for (int j = 0; j < Src::kA; ++j) {
+  for (int j = 0; j < C::nA; ++j) {
     const int r = 8 * (wave + W * j) + (lane >> 3);
     const int rr = min(r, rows - 1);
     const int ar = FC1 ? a.perm[row0 + rr] / a.top_k : row0 + rr;
@@ -253,7 +278,7 @@ __global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(W / 2
   }
   // codes / scales this lane copies: row block 2(wave + W j) + lane/32, chunk or dword lane%32
 #pragma unroll
-  for (int j = 0; j < Src::kB; ++j) {
+  for (int j = 0; j < C::nB; ++j) {
     const int blk = nb0 + 2 * (wave + W * j) + (lane >> 5);
     src.b[j] = a.codes + ((size_t)e * M.nb + blk) * M.kb * kTileBytes + (lane & 31) * 16;
     src.s[j] = a.scales + ((size_t)e * M.nb + blk) * M.kb4 * kScaleGroupBytes + (lane & 31) * 4;
@@ -268,20 +293,17 @@ __global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(W / 2
       for (int i = 0; i < 16; ++i) acc[mi][nj][i] = 0.f;
 
   const int S = 2 * M.kb;    // stages
-  if constexpr (MI == 4) {   // W = 4: every wave holds row 0, so live >= 1
+  if constexpr (MI == 4) {
     switch (live) {
-      case 1: k_loop<BM, W, MI, 1>(smem, src, S, wave, wn, r0, lane, acc); break;
-      case 2: k_loop<BM, W, MI, 2>(smem, src, S, wave, wn, r0, lane, acc); break;
-      case 3: k_loop<BM, W, MI, 3>(smem, src, S, wave, wn, r0, lane, acc); break;
-      default: k_loop<BM, W, MI, 4>(smem, src, S, wave, wn, r0, lane, acc); break;
+      case 1: k_loop<C, 1>(smem, src, S, wave, lane, acc); break;
+      case 2: k_loop<C, 2>(smem, src, S, wave, lane, acc); break;
+      case 3: k_loop<C, 3>(smem, src, S, wave, lane, acc); break;
+      default: k_loop<C, 4>(smem, src, S, wave, lane, acc); break;
     }
   } else {
     switch (live) {
-      case 0:
-        if constexpr (W > 4) k_loop<BM, W, MI, 0>(smem, src, S, wave, wn, r0, lane, acc);
-        break;
-      case 1: k_loop<BM, W, MI, 1>(smem, src, S, wave, wn, r0, lane, acc); break;
-      default: k_loop<BM, W, MI, 2>(smem, src, S, wave, wn, r0, lane, acc); break;
+      case 1: k_loop<C, 1>(smem, src, S, wave, lane, acc); break;
+      default: k_loop<C, 2>(smem, src, S, wave, lane, acc); break;
     }
   }
   const int n32 = lane & 31, h = lane >> 5;
@@ -294,38 +316,47 @@ __global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(W / 2
     for (int nj = 0; nj < NJ; ++nj) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int r = r0 + mi * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
+        const int r = mi * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
         const float v = acc[mi][nj][i];
         if constexpr (FC1) {
           // columns 0..15 of the block pair are gate j, 16..31 up j (interleaved row blocks)
           const float u = __shfl_xor(v, 16, kWave);
           if (n32 < 16 && r < rows) {
-            const int j = (nb0 + wn * (2 * NJ) + 2 * nj) >> 1;
+            const int j = (nb0 + wave * (2 * NJ) + 2 * nj) >> 1;
             static_cast<uint16_t*>(a.out)[(size_t)(row0 + r) * a.ldo + j * kTileN + n32] =
                 f32_to_bf16_rne(silu_f32(v) * u);
           }
         } else {
           if (r < rows)
-            static_cast<float*>(a.out)[(size_t)(row0 + r) * a.ldo + (size_t)(nb0 + wn * (2 * NJ) + 2 * nj) * kTileN +
-                                       n32] = v;
+            static_cast<float*>(a.out)[(size_t)(row0 + r) * a.ldo +
+                                       (size_t)(nb0 + wave * (2 * NJ) + 2 * nj) * kTileN + n32] = v;
         }
       }
     }
   }
 }
 
-#ifndef MOE_PREFILL_WAVES
-#define MOE_PREFILL_WAVES 4
+#ifndef MOE_PREFILL_WN
+#define MOE_PREFILL_WN 4
 #endif
 
-template <bool FC1, int BM>
-hipError_t launch_pre(const FcArgs& a, int tiles_max, hipStream_t stream) {
-  constexpr int W = BM == 128 ? MOE_PREFILL_WAVES : 4;
-  const int slices = a.mat.nb / kBlocks;
+template <bool FC1, int BM, int W>
+hipError_t launch_cfg(const FcArgs& a, int tiles_max, hipStream_t stream) {
+  using C = Cfg<BM, W>;
+  const int slices = a.mat.nb / C::kBlocks;
   const long long items = (long long)((tiles_max + kTileGroup - 1) / kTileGroup * kTileGroup) * slices;
   const long long grid = (items + 7) / 8 * 8;
   hipLaunchKernelGGL((fc_pre<FC1, BM, W>), dim3((unsigned)grid), dim3(W * kWave), 0, stream, a, slices);
   return hipGetLastError();
+}
+
+template <bool FC1, int BM>
+hipError_t launch_pre(const FcArgs& a, int tiles_max, hipStream_t stream) {
+  // 512-column workgroups where chosen and N allows (N a multiple of 512), else 256
+  if constexpr (BM == 128 && MOE_PREFILL_WN == 8) {
+    if (a.mat.nb % Cfg<BM, 8>::kBlocks == 0) return launch_cfg<FC1, BM, 8>(a, tiles_max, stream);
+  }
+  return launch_cfg<FC1, BM, 4>(a, tiles_max, stream);
 }
 
 }  // namespace
