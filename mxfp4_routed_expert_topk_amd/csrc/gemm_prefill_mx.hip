@@ -36,6 +36,8 @@
 // FC1: row blocks come in (gate j, up j) pairs (interleaved repack); the
 // epilogue stores h = silu(g) * u in fp32 for the MXFP8 requantisation.  FC2:
 // fp32 y rows in route-row order.
+#include <type_traits>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -99,9 +101,20 @@ __device__ __forceinline__ void wait_groups(int ahead, int na) {
 static_assert(kDepth >= 1 && kDepth <= 8, "wait_ahead covers up to seven stage groups behind the current one");
 static_assert(7 * (kCopySlots + 2 * kNBW) <= 63, "vmcnt holds at most 63");
 
+// Stages s0 + P .. s0 + N - 1 that lie below s0 + n, ring slots P .. N - 1.
+template <int P, int N, class F>
+__device__ __forceinline__ void ring_pass(F& f, int s0, int n) {
+  if constexpr (P < N) {
+    if (P < n) {
+      f(std::integral_constant<int, P>{}, s0 + P);
+      ring_pass<P + 1, N>(f, s0, n);
+    }
+  }
+}
+
 template <bool FC1, int LIVE>
-__device__ __forceinline__ void tile_body(const FcArgs& a, uint8_t* sa, uint8_t* ss, int e, int row0, int rows,
-                                          int slice) {
+__device__ __forceinline__ void tile_body(const FcArgs& a, uint8_t* sa, uint8_t* ss, const int* srow, int e,
+                                          int row0, int rows, int slice) {
   constexpr int MB = 2 * LIVE;            // 16-row MFMA blocks
   constexpr int GROUPS = 4 * LIVE;        // 8-row copy groups of the live rows
   const int t = threadIdx.x, lane = t & 63;
@@ -124,7 +137,7 @@ __device__ __forceinline__ void tile_body(const FcArgs& a, uint8_t* sa, uint8_t*
   for (int j = 0; j < kCopySlots; ++j) {
     const int r = 8 * (wave + kWaves * j) + (lane >> 3);
     const int rr = min(r, rows - 1);
-    const int ar = FC1 ? a.perm[row0 + rr] / a.top_k : row0 + rr;
+    const int ar = FC1 ? srow[rr] : row0 + rr;
     aoff[j] = (uint32_t)ar * (uint32_t)a.lda + swz(lane & 7, r) * 16;
   }
   // scale copy, once per tile: the live rows' E8M0 bytes, row-major with
@@ -140,7 +153,7 @@ __device__ __forceinline__ void tile_body(const FcArgs& a, uint8_t* sa, uint8_t*
       const int byte = 4 * (kWave * i + lane);
       const int r = byte / sgroups;
       const int rr = min(r, rows - 1);
-      const int ar = FC1 ? a.perm[row0 + rr] / a.top_k : row0 + rr;
+      const int ar = FC1 ? srow[rr] : row0 + rr;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rascl, (lds_void_t*)(ss + i * 4 * kWave), 4,
                                                (uint32_t)ar * (uint32_t)sgroups + (byte - r * sgroups), 0, 0, 0);
     }
@@ -160,25 +173,39 @@ __device__ __forceinline__ void tile_body(const FcArgs& a, uint8_t* sa, uint8_t*
 #pragma unroll
     for (int j = 0; j < kNBW; ++j) acc[mb][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  u32x4_t bq[kDepth][kNBW];
-  uint32_t bs[kDepth][kNBW];
+  // weight ring: stage st in slot st % kRing; stage st + kDepth is loaded at
+  // the top of stage st into the slot stage st-1 has just finished with
+  constexpr int kRing = kDepth + 1;
+  u32x4_t bq[kRing][kNBW];
+  uint32_t bs[kRing][kNBW];
 
-  auto issue_lds = [&](int s) {
-    uint8_t* buf = sa + (s % kBufs) * kStageBytes;
+  // Stage s >= S (the loads issued "past the end", see run_stage): the
+  // per-lane offset is set to kPastEnd and the scalar one to 0, which puts the
+  // address beyond its buffer resource's range (the range check takes the
+  // per-lane offset; every resource here is under 2^31 bytes): the load
+  // returns zeros without a memory request and still counts in vmcnt, which
+  // is all it is there for.
+  constexpr uint32_t kPastEnd = 0x80000000u;
+  // activation copies of stage s into stage buffer `bi`
+  auto issue_lds = [&](int bi, int s) {
+    uint8_t* buf = sa + bi * kStageBytes;
+    const bool real = s < S;
 #pragma unroll
     for (int j = 0; j < kCopySlots; ++j)
-      if (j < na)
+      if (kWaves == 4 ? j < LIVE : j < na)   // four waves: every wave copies LIVE groups, a constant
         __builtin_amdgcn_raw_ptr_buffer_load_lds(racts, (lds_void_t*)(buf + (wave + kWaves * j) * 1024), 16,
-                                                 aoff[j], s * kTileK, 0, 0);
+                                                 real ? aoff[j] : kPastEnd, real ? s * kTileK : 0, 0, 0);
   };
   auto load_regs = [&](u32x4_t (&q)[kNBW], uint32_t (&sb)[kNBW], int s) {
+    const bool real = s < S;
 #pragma unroll
     for (int j = 0; j < kNBW; ++j)
-      q[j] = __builtin_amdgcn_raw_buffer_load_b128(rcode, lane * 16, j * bstride + s * kTileBytes, 0);
+      q[j] = __builtin_amdgcn_raw_buffer_load_b128(rcode, real ? lane * 16 : kPastEnd,
+                                                   real ? j * bstride + s * kTileBytes : 0, 0);
 #pragma unroll
     for (int j = 0; j < kNBW; ++j)
-      sb[j] = __builtin_amdgcn_raw_buffer_load_b8(rscale, lane * 4,
-                                                  j * sstride + (s >> 2) * kScaleGroupBytes + (s & 3), 0);
+      sb[j] = __builtin_amdgcn_raw_buffer_load_b8(
+          rscale, real ? lane * 4 : kPastEnd, real ? j * sstride + (s >> 2) * kScaleGroupBytes + (s & 3) : 0, 0);
   };
 
   // A operand position of this lane inside a staged 16-row block
@@ -187,46 +214,59 @@ __device__ __forceinline__ void tile_body(const FcArgs& a, uint8_t* sa, uint8_t*
   const int hi_off = rl * kTileK + swz(4 + q, rl) * 16;
   const int s_off = rl * sgroups + q;
 
+  // Every stage issues the same loads -- one group: this wave's activation
+  // copies and weight loads of stage st + kDepth (past the end: zero loads
+  // into the buffer and ring slot of stage st-1, which no later stage
+  // reads) -- so the wait at each stage counts them exactly,
+  // and the compiler, seeing the same operations on every path around the
+  // loop, places its own waits for the weight registers no earlier than that.
+  auto run_stage = [&](auto pc, int st) {
+    constexpr int p = decltype(pc)::value;   // ring slot of stage st
+    // this wave's loads of stage st have landed (the kDepth - 1 groups after
+    // it may still be in flight) and its LDS reads of stage st-1 have
+    // returned; the barrier extends both to every wave
+    if constexpr (kWaves == 4) MOE_WAIT_VM_LGKM((kDepth - 1) * (LIVE + 2 * kNBW));   // na == LIVE
+    else wait_groups<2 * kNBW>(kDepth - 1, na);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    issue_lds((st + kDepth) % kBufs, st + kDepth);   // into the buffer of stage st-1
+    load_regs(bq[(p + kDepth) % kRing], bs[(p + kDepth) % kRing], st + kDepth);
+    const uint8_t* cur = sa + (st % kBufs) * kStageBytes;
+    const uint8_t* curs = ss + 4 * st;
 #pragma unroll
-  for (int d = 0; d < kDepth; ++d)
-    if (d < S) {
-      issue_lds(d);
-      load_regs(bq[d], bs[d], d);
-    }
-
-  for (int s0 = 0; s0 < S; s0 += kDepth) {
+    for (int mb = 0; mb < MB; ++mb) {
+      const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(cur + mb * 16 * kTileK + lo_off);
+      const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(cur + mb * 16 * kTileK + hi_off);
+      const int sc = curs[mb * 16 * sgroups + s_off];
+      const i32x8_t Af = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                          (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
 #pragma unroll
-    for (int p = 0; p < kDepth; ++p) {
-      const int st = s0 + p;
-      if (st < S) {
-        // this wave's loads of stage st have landed (those of the stages after
-        // it may still be in flight) and its LDS reads of stage st-1 have
-        // returned; the barrier extends both to every wave
-        wait_groups<2 * kNBW>(min(kDepth - 1, S - 1 - st), na);
-        asm volatile("" ::: "memory");
-        __builtin_amdgcn_s_barrier();
-        asm volatile("" ::: "memory");
-        if (st + kDepth < S) issue_lds(st + kDepth);   // into the buffers of stage st-1
-        const uint8_t* cur = sa + (st % kBufs) * kStageBytes;
-        const uint8_t* curs = ss + 4 * st;
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-          const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(cur + mb * 16 * kTileK + lo_off);
-          const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(cur + mb * 16 * kTileK + hi_off);
-          const int sc = curs[mb * 16 * sgroups + s_off];
-          const i32x8_t Af = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
-                              (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-#pragma unroll
-          for (int j = 0; j < kNBW; ++j) {
-            const i32x8_t Bf = {(int)bq[p][j][0], (int)bq[p][j][1], (int)bq[p][j][2], (int)bq[p][j][3], 0, 0, 0, 0};
-            acc[mb][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(Af, Bf, acc[mb][j], 0, 4, 0, sc, 0,
-                                                                          (int)bs[p][j]);
-          }
-        }
-        if (st + kDepth < S) load_regs(bq[p], bs[p], st + kDepth);
+      for (int j = 0; j < kNBW; ++j) {
+        const i32x8_t Bf = {(int)bq[p][j][0], (int)bq[p][j][1], (int)bq[p][j][2], (int)bq[p][j][3], 0, 0, 0, 0};
+        acc[mb][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(Af, Bf, acc[mb][j], 0, 4, 0, sc, 0,
+                                                                      (int)bs[p][j]);
       }
     }
+    // The stage's MFMAs stay above the next barrier (this empty statement
+    // reads their results), so their ring slot is free when the next stage's
+    // loads overwrite it: no second register set and no copies (a copy of a
+    // register still being loaded would make the compiler wait for the load).
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) asm volatile("" ::"v"(acc[mb][0]), "v"(acc[mb][kNBW - 1]));
+  };
+
+#pragma unroll
+  for (int d = 0; d < kDepth; ++d) {
+    issue_lds(d, d);
+    load_regs(bq[d], bs[d], d);
   }
+  int s0 = 0;
+  for (; s0 + kRing <= S; s0 += kRing) ring_pass<0, kRing>(run_stage, s0, kRing);
+  ring_pass<0, kRing - 1>(run_stage, s0, S - s0);   // the last S % kRing stages
+  // the last stages' zero copies still write LDS: drain them before the
+  // workgroup can end and its LDS be handed to the next one
+  MOE_WAIT_VM_LGKM(0);
 
   // ---- epilogue.  16x16 D layout: lane holds column l%16, rows 4(l/16) + i.
 #pragma unroll
@@ -250,6 +290,7 @@ template <bool FC1>
 __global__ __launch_bounds__(kWaves * kWave, 8 / kWaves) void fc_pre_mx(FcArgs a, int slices) {
   __shared__ __align__(1024) uint8_t sa[kBufs * kStageBytes];
   extern __shared__ __align__(16) uint8_t ss[];   // kRows * K/32 bytes (launch size)
+  __shared__ int srow[kRows];                      // source row of each tile row
   const int ntiles = *a.tile_count;
   const int total = (ntiles + kTileGroup - 1) / kTileGroup * kTileGroup * slices;   // whole groups
   // eight contiguous chunks of the (tile, slice) list, one per XCD; within it
@@ -266,11 +307,18 @@ __global__ __launch_bounds__(kWaves * kWave, 8 / kWaves) void fc_pre_mx(FcArgs a
   const int2 td = a.tiles[tile];
   const int e = td.x, row0 = td.y;
   const int rows = min(kRows, a.offsets[e + 1] - row0);
+  // FC1: the tile's source rows (through the route permutation), loaded once
+  // in parallel: the copy address loops below then read them from LDS
+  // instead of waiting on one global load per copy
+  if constexpr (FC1) {
+    if (threadIdx.x < kRows) srow[threadIdx.x] = a.perm[row0 + min((int)threadIdx.x, rows - 1)] / a.top_k;
+    __syncthreads();
+  }
   switch ((rows + 31) >> 5) {
-    case 1: tile_body<FC1, 1>(a, sa, ss, e, row0, rows, slice); break;
-    case 2: tile_body<FC1, 2>(a, sa, ss, e, row0, rows, slice); break;
-    case 3: tile_body<FC1, 3>(a, sa, ss, e, row0, rows, slice); break;
-    default: tile_body<FC1, 4>(a, sa, ss, e, row0, rows, slice); break;
+    case 1: tile_body<FC1, 1>(a, sa, ss, srow, e, row0, rows, slice); break;
+    case 2: tile_body<FC1, 2>(a, sa, ss, srow, e, row0, rows, slice); break;
+    case 3: tile_body<FC1, 3>(a, sa, ss, srow, e, row0, rows, slice); break;
+    default: tile_body<FC1, 4>(a, sa, ss, srow, e, row0, rows, slice); break;
   }
 }
 
