@@ -9,23 +9,23 @@
 // holds 23.4 MB of codes and scales at hidden 7168 / intermediate 2048, while
 // its ~85 routed rows of E4M3 activations hold 0.6 MB), so one tile covers
 // every row an expert has in a balanced batch and each weight byte is read
-// once.  A workgroup of kWaves waves (four by default: two workgroups per CU,
-// whose stage barriers fall at different times) runs one stage per 128-K
-// column block:
+// once.  A workgroup of kWaves waves (four by default; three workgroups fit
+// a CU, whose stage barriers fall at different times) runs one stage per
+// 128-K column block, loading stage st + kDepth while stage st multiplies:
 //  * weights: the repacked 1 KB tile is already the MFMA's B operand (lane l
 //    holds the 32 codes of row l%16, K group l/16), so each wave loads its two
-//    row blocks straight into registers, kDepth stages ahead, with their E8M0
-//    bytes (buffer loads: one VGPR offset, SGPR bases);
+//    row blocks straight into registers, with their E8M0 bytes, into a ring
+//    of kDepth + 1 register sets (buffer loads: one VGPR offset, SGPR bases);
 //  * activations: the tile's rows (gathered through the route permutation
 //    for FC1) are shared by the waves, so they are copied global->LDS by
-//    buffer_load ... lds, kDepth stages ahead, into 128-byte rows under the
-//    same conflict-free chunk swizzle as the bf16 prefill kernel; each lane
-//    reads its A operand (bytes 16(l/16).. and 64+16(l/16).. of row l%16)
-//    with two ds_read_b128.  Their E8M0 bytes (K/32 per row, 28 KB per tile
-//    at hidden 7168, dynamic LDS) are copied once per tile with whole-row
-//    dword requests, and each lane reads its byte (K group l/16) with one
-//    ds_read_u8: per-stage copies of four bytes per row would cost a cache
-//    line request each.
+//    buffer_load ... lds into 128-byte rows under the same conflict-free
+//    chunk swizzle as the bf16 prefill kernel; each lane reads its A operand
+//    (bytes 16(l/16).. and 64+16(l/16).. of row l%16) with two ds_read_b128.
+//    Each row's four E8M0 bytes of the stage follow the rows as one dword
+//    per row (half-wave dword copies, one per wave), read with ds_read_u8.
+// Every stage issues the same group of loads (past the end: zero loads with
+// an out-of-range offset), so the wait before each stage counts them exactly
+// and the compiler never waits for weights still in flight at the MFMAs.
 // Each wave owns all rows x 32 columns (one gate/up pair for FC1): 2*LIVE
 // 16-row blocks by two row blocks; 32-row blocks wholly past the tile's rows
 // are neither copied nor multiplied.
@@ -60,7 +60,9 @@ static_assert(kWaves == 4 || kWaves == 8, "four or eight waves per workgroup");
 #endif
 constexpr int kDepth = MOE_MX_DEPTH;        // stages loaded ahead of the one multiplied
 constexpr int kBufs = kDepth + 1;           // LDS stage buffers
-constexpr int kStageBytes = kRows * kTileK;   // 128 rows x 128 E4M3
+constexpr int kStageA = kRows * kTileK;       // 128 rows x 128 E4M3
+constexpr int kStageBytes = kStageA + kRows * 4;   // + each row's four E8M0 bytes of the stage
+constexpr int kScaleLanes = kRows / kWaves;        // rows whose scale dword one wave copies
 constexpr int kRsrcWord3 = 0x00020000;        // raw buffer, 32-bit data format
 #ifndef MOE_PREFILL_TILE_GROUP
 #define MOE_PREFILL_TILE_GROUP 1
@@ -99,7 +101,7 @@ __device__ __forceinline__ void wait_groups(int ahead, int na) {
   }
 }
 static_assert(kDepth >= 1 && kDepth <= 8, "wait_ahead covers up to seven stage groups behind the current one");
-static_assert(7 * (kCopySlots + 2 * kNBW) <= 63, "vmcnt holds at most 63");
+static_assert(7 * (kCopySlots + 1 + 2 * kNBW) <= 63, "vmcnt holds at most 63");
 
 // Stages s0 + P .. s0 + N - 1 that lie below s0 + n, ring slots P .. N - 1.
 template <int P, int N, class F>
@@ -113,8 +115,7 @@ __device__ __forceinline__ void ring_pass(F& f, int s0, int n) {
 }
 
 template <bool FC1, int LIVE>
-__device__ __forceinline__ void tile_body(const FcArgs& a, uint8_t* sa, uint8_t* ss, const int* srow, int e,
-                                          int row0, int rows, int slice) {
+__device__ __forceinline__ void tile_body(const FcArgs& a, uint8_t* sa, int e, int row0, int rows, int slice) {
   constexpr int MB = 2 * LIVE;            // 16-row MFMA blocks
   constexpr int GROUPS = 4 * LIVE;        // 8-row copy groups of the live rows
   const int t = threadIdx.x, lane = t & 63;
@@ -137,26 +138,17 @@ __device__ __forceinline__ void tile_body(const FcArgs& a, uint8_t* sa, uint8_t*
   for (int j = 0; j < kCopySlots; ++j) {
     const int r = 8 * (wave + kWaves * j) + (lane >> 3);
     const int rr = min(r, rows - 1);
-    const int ar = FC1 ? srow[rr] : row0 + rr;
+    const int ar = FC1 ? a.perm[row0 + rr] / a.top_k : row0 + rr;
     aoff[j] = (uint32_t)ar * (uint32_t)a.lda + swz(lane & 7, r) * 16;
   }
-  // scale copy, once per tile: the live rows' E8M0 bytes, row-major with
-  // sgroups bytes per row (a multiple of 4), as 64-dword copies spread over
-  // the waves; lane L of copy i fills dword 64 i + L.  Issued before the
-  // first stage's loads, so the first stage's wait covers them.
+  // scale copy of each stage: lane L < kScaleLanes of wave w copies the
+  // stage's four E8M0 bytes (one dword: sgroups is a multiple of 4) of row
+  // kScaleLanes w + L to dword (kScaleLanes w + L) after the stage's rows
+  uint32_t soff;
   {
-    // rounded up: the last copy may run past the live rows (their bytes are
-    // never read; 32 LIVE sgroups is a multiple of 128, so it ends inside the
-    // 128 sgroups bytes of ss)
-    const int copies = (32 * LIVE * sgroups + 4 * kWave - 1) / (4 * kWave);
-    for (int i = wave; i < copies; i += kWaves) {
-      const int byte = 4 * (kWave * i + lane);
-      const int r = byte / sgroups;
-      const int rr = min(r, rows - 1);
-      const int ar = FC1 ? srow[rr] : row0 + rr;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rascl, (lds_void_t*)(ss + i * 4 * kWave), 4,
-                                               (uint32_t)ar * (uint32_t)sgroups + (byte - r * sgroups), 0, 0, 0);
-    }
+    const int rr = min(kScaleLanes * wave + (lane & (kScaleLanes - 1)), rows - 1);
+    const int ar = FC1 ? a.perm[row0 + rr] / a.top_k : row0 + rr;
+    soff = (uint32_t)ar * (uint32_t)sgroups;
   }
   // this wave's two weight row blocks, as buffer resources sized to them
   const int nb0 = slice * kBlocks + wave * kNBW;
@@ -195,6 +187,9 @@ __device__ __forceinline__ void tile_body(const FcArgs& a, uint8_t* sa, uint8_t*
       if (kWaves == 4 ? j < LIVE : j < na)   // four waves: every wave copies LIVE groups, a constant
         __builtin_amdgcn_raw_ptr_buffer_load_lds(racts, (lds_void_t*)(buf + (wave + kWaves * j) * 1024), 16,
                                                  real ? aoff[j] : kPastEnd, real ? s * kTileK : 0, 0, 0);
+    if (lane < kScaleLanes)   // part of the wave: one operation all the same
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rascl, (lds_void_t*)(buf + kStageA + kScaleLanes * 4 * wave), 4,
+                                               real ? soff : kPastEnd, real ? 4 * s : 0, 0, 0);
   };
   auto load_regs = [&](u32x4_t (&q)[kNBW], uint32_t (&sb)[kNBW], int s) {
     const bool real = s < S;
@@ -212,7 +207,6 @@ __device__ __forceinline__ void tile_body(const FcArgs& a, uint8_t* sa, uint8_t*
   const int rl = lane & 15, q = lane >> 4;
   const int lo_off = rl * kTileK + swz(q, rl) * 16;
   const int hi_off = rl * kTileK + swz(4 + q, rl) * 16;
-  const int s_off = rl * sgroups + q;
 
   // Every stage issues the same loads -- one group: this wave's activation
   // copies and weight loads of stage st + kDepth (past the end: zero loads
@@ -225,20 +219,20 @@ __device__ __forceinline__ void tile_body(const FcArgs& a, uint8_t* sa, uint8_t*
     // this wave's loads of stage st have landed (the kDepth - 1 groups after
     // it may still be in flight) and its LDS reads of stage st-1 have
     // returned; the barrier extends both to every wave
-    if constexpr (kWaves == 4) MOE_WAIT_VM_LGKM((kDepth - 1) * (LIVE + 2 * kNBW));   // na == LIVE
-    else wait_groups<2 * kNBW>(kDepth - 1, na);
+    if constexpr (kWaves == 4) MOE_WAIT_VM_LGKM((kDepth - 1) * (LIVE + 1 + 2 * kNBW));   // na == LIVE
+    else wait_groups<1 + 2 * kNBW>(kDepth - 1, na);
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     issue_lds((st + kDepth) % kBufs, st + kDepth);   // into the buffer of stage st-1
     load_regs(bq[(p + kDepth) % kRing], bs[(p + kDepth) % kRing], st + kDepth);
     const uint8_t* cur = sa + (st % kBufs) * kStageBytes;
-    const uint8_t* curs = ss + 4 * st;
+    const uint8_t* curs = cur + kStageA;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
       const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(cur + mb * 16 * kTileK + lo_off);
       const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(cur + mb * 16 * kTileK + hi_off);
-      const int sc = curs[mb * 16 * sgroups + s_off];
+      const int sc = curs[(mb * 16 + rl) * 4 + q];
       const i32x8_t Af = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
                           (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
 #pragma unroll
@@ -289,8 +283,6 @@ __device__ __forceinline__ void tile_body(const FcArgs& a, uint8_t* sa, uint8_t*
 template <bool FC1>
 __global__ __launch_bounds__(kWaves * kWave, 8 / kWaves) void fc_pre_mx(FcArgs a, int slices) {
   __shared__ __align__(1024) uint8_t sa[kBufs * kStageBytes];
-  extern __shared__ __align__(16) uint8_t ss[];   // kRows * K/32 bytes (launch size)
-  __shared__ int srow[kRows];                      // source row of each tile row
   const int ntiles = *a.tile_count;
   const int total = (ntiles + kTileGroup - 1) / kTileGroup * kTileGroup * slices;   // whole groups
   // eight contiguous chunks of the (tile, slice) list, one per XCD; within it
@@ -307,18 +299,11 @@ __global__ __launch_bounds__(kWaves * kWave, 8 / kWaves) void fc_pre_mx(FcArgs a
   const int2 td = a.tiles[tile];
   const int e = td.x, row0 = td.y;
   const int rows = min(kRows, a.offsets[e + 1] - row0);
-  // FC1: the tile's source rows (through the route permutation), loaded once
-  // in parallel: the copy address loops below then read them from LDS
-  // instead of waiting on one global load per copy
-  if constexpr (FC1) {
-    if (threadIdx.x < kRows) srow[threadIdx.x] = a.perm[row0 + min((int)threadIdx.x, rows - 1)] / a.top_k;
-    __syncthreads();
-  }
   switch ((rows + 31) >> 5) {
-    case 1: tile_body<FC1, 1>(a, sa, ss, srow, e, row0, rows, slice); break;
-    case 2: tile_body<FC1, 2>(a, sa, ss, srow, e, row0, rows, slice); break;
-    case 3: tile_body<FC1, 3>(a, sa, ss, srow, e, row0, rows, slice); break;
-    default: tile_body<FC1, 4>(a, sa, ss, srow, e, row0, rows, slice); break;
+    case 1: tile_body<FC1, 1>(a, sa, e, row0, rows, slice); break;
+    case 2: tile_body<FC1, 2>(a, sa, e, row0, rows, slice); break;
+    case 3: tile_body<FC1, 3>(a, sa, e, row0, rows, slice); break;
+    default: tile_body<FC1, 4>(a, sa, e, row0, rows, slice); break;
   }
 }
 
@@ -327,8 +312,7 @@ hipError_t launch(const FcArgs& a, int tiles_max, hipStream_t stream) {
   const int slices = a.mat.nb / kBlocks;
   const long long items = (long long)((tiles_max + kTileGroup - 1) / kTileGroup * kTileGroup) * slices;
   const long long grid = (items + 7) / 8 * 8;
-  const size_t scale_bytes = (size_t)kRows * (a.lda / 32);
-  hipLaunchKernelGGL((fc_pre_mx<FC1>), dim3((unsigned)grid), dim3(kWaves * kWave), scale_bytes, stream, a, slices);
+  hipLaunchKernelGGL((fc_pre_mx<FC1>), dim3((unsigned)grid), dim3(kWaves * kWave), 0, stream, a, slices);
   return hipGetLastError();
 }
 
