@@ -141,7 +141,28 @@ class Batches:
         return {"ms_per_step": ms, "ms_per_step_with_events": float(stage.sum(axis=1).mean()),
                 "stage_ms": stage.mean(axis=0), "fc1_ms": stage[:, 1],
                 "layer_bytes": alg[:, 0].mean(), "fc1_bytes": alg[:, 1].mean(), "flops": alg[:, 2].mean(),
-                "graph_ms_per_step": self.run_graph(steps, warmup)}
+                "graph_ms_per_step": self.run_graph(steps, warmup),
+                "fused_ms_per_step": self.run_fused(steps, warmup)}
+
+    def run_fused(self, steps, warmup):
+        """The same steps through the one-launch forward (bf16, at most 256
+        routes), or None where it does not apply."""
+        import torch
+        if self.base.act != "bf16" or self.T * self.k > 256:
+            return None
+        for j in range(warmup):
+            x, ids, wts = self.inputs[j % len(self.inputs)]
+            self.plan.forward_fused(x, ids, wts, out=self.out, acc=self.acc)
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record()
+        for j in range(steps):
+            x, ids, wts = self.inputs[(warmup + j) % len(self.inputs)]
+            self.plan.forward_fused(x, ids, wts, out=self.out, acc=self.acc)
+        end.record()
+        torch.cuda.synchronize()
+        self.plan.fused_status()   # every wait of the last call completed
+        return start.elapsed_time(end) / steps
 
     def run_graph(self, steps, warmup):
         """The same steps replayed from one captured hipGraph per input set (the
@@ -182,7 +203,10 @@ class Batches:
                 "stage_us": {k: round(float(v) * 1e3, 2) for k, v in zip(STAGES, r["stage_ms"])},
                 "us_per_step_with_stage_events": round(r["ms_per_step_with_events"] * 1e3, 2),
                 "graph_us_per_step": round(r["graph_ms_per_step"] * 1e3, 2),
-                "graph_tokens_per_s": round(self.T / (r["graph_ms_per_step"] * 1e-3), 1)}
+                "graph_tokens_per_s": round(self.T / (r["graph_ms_per_step"] * 1e-3), 1),
+                **({"fused_us_per_step": round(r["fused_ms_per_step"] * 1e3, 2),
+                    "fused_tokens_per_s": round(self.T / (r["fused_ms_per_step"] * 1e-3), 1)}
+                   if r.get("fused_ms_per_step") else {})}
 
 
 # FC1 kernel source of each workload (the counter records hash it with the shared header)

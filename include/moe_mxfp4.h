@@ -52,7 +52,8 @@ typedef enum {
   MOE_ERR_SCALE_BYTE = 5,   /* a weight scale byte is not accepted (plan) */
   MOE_ERR_WORKSPACE = 6,    /* workspace or repacked buffer too small */
   MOE_ERR_UNSUPPORTED = 7,  /* device is not gfx950 */
-  MOE_ERR_HIP = 8           /* a HIP runtime call failed (text from hipGetErrorString) */
+  MOE_ERR_HIP = 8,          /* a HIP runtime call failed (text from hipGetErrorString) */
+  MOE_ERR_TIMEOUT = 9       /* a wait of a fused forward passed its time bound (moe_mxfp4_fused_status) */
 } moe_status;
 
 typedef enum {
@@ -111,6 +112,37 @@ moe_status moe_mxfp4_forward(moe_mxfp4_plan_t plan, const uint16_t* hidden,
                              const int32_t* topk_ids, const float* topk_weights,
                              int32_t num_tokens, float* acc_fp32, uint16_t* out_bf16,
                              void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* The same forward as moe_mxfp4_forward, the whole layer in one kernel
+ * launch, for decode-sized batches: a MOE_ACT_BF16 plan and at most 256 routes
+ * (num_tokens * top_k), else MOE_ERR_SHAPE.  The pages' fused MoE launch
+ * (pegainfer PR #867: dispatch, FC1, activation, FC2 and combine in one kernel)
+ * is the model; here every workgroup routes the batch itself and the FC2 and
+ * combine work waits on counters of the work it reads.  Arguments, ownership
+ * and outputs are those of moe_mxfp4_forward.  It always runs the 16-row
+ * streaming kernels' arithmetic: where moe_mxfp4_forward takes those too
+ * (fewer than 16 routes per resident expert, or hidden not a multiple of 256)
+ * the outputs are bitwise equal; otherwise both meet the same tolerance of the
+ * exact result.  Differences:
+ *  - the launch is cooperative (every workgroup resident at once), which HIP
+ *    graph capture may not accept: use moe_mxfp4_forward under capture;
+ *  - the workspace holds the counters: it must be zero before the first fused
+ *    forward that uses it (a zero-filled workspace is ready; the calls keep it
+ *    consistent afterwards), and concurrent calls sharing one workspace race;
+ *  - each wait is bounded in time (100 ms, or MOE_FUSED_SPIN_TICKS ticks of the
+ *    100 MHz device clock from the environment); past the bound the kernel
+ *    still ends, its outputs are not valid and moe_mxfp4_fused_status reports
+ *    MOE_ERR_TIMEOUT.
+ * Enqueue-only: no host synchronisation and no allocation. */
+moe_status moe_mxfp4_forward_fused(moe_mxfp4_plan_t plan, const uint16_t* hidden,
+                                   const int32_t* topk_ids, const float* topk_weights,
+                                   int32_t num_tokens, float* acc_fp32, uint16_t* out_bf16,
+                                   void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Whether the plan's last moe_mxfp4_forward_fused on this workspace completed
+ * every wait: MOE_OK, or MOE_ERR_TIMEOUT.  Synchronises the stream. */
+moe_status moe_mxfp4_fused_status(moe_mxfp4_plan_t plan, void* workspace, size_t workspace_bytes,
+                                  hipStream_t stream);
 
 /* Route metadata only (the first stage of forward), for checking:
  *   counts  [E] int32, offsets [E+1] int32 (exclusive prefix sum of counts),

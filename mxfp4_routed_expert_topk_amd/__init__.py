@@ -27,10 +27,11 @@ LIB_PATH = os.path.join(HERE, "libmoe_mxfp4.so")
 MOE_ACT_BF16 = 0
 MOE_ACT_MXFP8 = 1
 STATUS_NAMES = {0: "MOE_OK", 1: "MOE_ERR_ARG", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_ALIGN", 4: "MOE_ERR_CAPACITY",
-                5: "MOE_ERR_SCALE_BYTE", 6: "MOE_ERR_WORKSPACE", 7: "MOE_ERR_UNSUPPORTED", 8: "MOE_ERR_HIP"}
-EXPORTS = ("moe_mxfp4_query_sizes", "moe_mxfp4_plan", "moe_mxfp4_forward", "moe_mxfp4_route",
-           "moe_mxfp8_quantize", "moe_router_topk", "moe_mxfp4_set_stage_events", "moe_mxfp4_destroy",
-           "moe_mxfp4_last_error")
+                5: "MOE_ERR_SCALE_BYTE", 6: "MOE_ERR_WORKSPACE", 7: "MOE_ERR_UNSUPPORTED", 8: "MOE_ERR_HIP",
+                9: "MOE_ERR_TIMEOUT"}
+EXPORTS = ("moe_mxfp4_query_sizes", "moe_mxfp4_plan", "moe_mxfp4_forward", "moe_mxfp4_forward_fused",
+           "moe_mxfp4_fused_status", "moe_mxfp4_route", "moe_mxfp8_quantize", "moe_router_topk",
+           "moe_mxfp4_set_stage_events", "moe_mxfp4_destroy", "moe_mxfp4_last_error")
 
 
 class MoeError(RuntimeError):
@@ -75,6 +76,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_mxfp4_query_sizes.argtypes = [cfgp, ctypes.POINTER(sz), ctypes.POINTER(sz)]
     lib.moe_mxfp4_plan.argtypes = [cfgp, vp, vp, vp, vp, vp, sz, vp, ctypes.POINTER(vp)]
     lib.moe_mxfp4_forward.argtypes = [vp, vp, vp, vp, i32, vp, vp, vp, sz, vp]
+    lib.moe_mxfp4_forward_fused.argtypes = [vp, vp, vp, vp, i32, vp, vp, vp, sz, vp]
+    lib.moe_mxfp4_fused_status.argtypes = [vp, vp, sz, vp]
     lib.moe_mxfp4_route.argtypes = [vp, vp, i32, vp, vp, vp, vp, vp, sz, vp]
     lib.moe_mxfp8_quantize.argtypes = [vp, i32, i32, vp, vp, vp]
     lib.moe_router_topk.argtypes = [vp, i32, i32, i32, vp, vp, vp]
@@ -83,8 +86,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_mxfp4_destroy.restype = None
     lib.moe_mxfp4_last_error.argtypes = []
     lib.moe_mxfp4_last_error.restype = ctypes.c_char_p
-    for name in ("moe_mxfp4_query_sizes", "moe_mxfp4_plan", "moe_mxfp4_forward", "moe_mxfp4_route",
-                 "moe_mxfp8_quantize", "moe_mxfp4_set_stage_events"):
+    for name in ("moe_mxfp4_query_sizes", "moe_mxfp4_plan", "moe_mxfp4_forward", "moe_mxfp4_forward_fused",
+                 "moe_mxfp4_fused_status", "moe_mxfp4_route", "moe_mxfp8_quantize", "moe_router_topk",
+                 "moe_mxfp4_set_stage_events"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -123,7 +127,8 @@ class Plan:
         self.repacked_bytes, self.workspace_bytes = query_sizes(cfg)
         dev = w13_codes.device
         self.repacked = torch.empty(self.repacked_bytes, dtype=torch.uint8, device=dev)
-        self.workspace = torch.empty(self.workspace_bytes, dtype=torch.uint8, device=dev)
+        # zero-filled: the fused forward keeps its counters here and starts from zeros
+        self.workspace = torch.zeros(self.workspace_bytes, dtype=torch.uint8, device=dev)
         h = ctypes.c_void_p()
         _check(lib.moe_mxfp4_plan(ctypes.byref(cfg.c()), _ptr(w13_codes), _ptr(w13_scales), _ptr(w2_codes),
                                   _ptr(w2_scales), _ptr(self.repacked), self.repacked_bytes, _stream(stream),
@@ -152,6 +157,24 @@ class Plan:
         _check(load_library().moe_mxfp4_forward(self._h, _ptr(hidden), _ptr(topk_ids), _ptr(topk_weights), T,
                                                 _ptr(acc), _ptr(out), _ptr(ws), ws.numel(), _stream(stream)))
         return out
+
+    def forward_fused(self, hidden, topk_ids, topk_weights, out=None, acc=None, num_tokens=None, stream=None,
+                      workspace=None):
+        """The same forward in one kernel launch (bf16 plans, at most 256 routes)."""
+        import torch
+        T = hidden.shape[0] if num_tokens is None else int(num_tokens)
+        if out is None:
+            out = torch.empty((hidden.shape[0], self.cfg.hidden), dtype=torch.bfloat16, device=hidden.device)
+        ws = self.workspace if workspace is None else workspace
+        _check(load_library().moe_mxfp4_forward_fused(self._h, _ptr(hidden), _ptr(topk_ids), _ptr(topk_weights),
+                                                      T, _ptr(acc), _ptr(out), _ptr(ws), ws.numel(),
+                                                      _stream(stream)))
+        return out
+
+    def fused_status(self, stream=None, workspace=None):
+        """Raise MoeError(MOE_ERR_TIMEOUT) if the last fused forward's waits timed out (synchronises)."""
+        ws = self.workspace if workspace is None else workspace
+        _check(load_library().moe_mxfp4_fused_status(self._h, _ptr(ws), ws.numel(), _stream(stream)))
 
     def route(self, topk_ids, num_tokens=None, stream=None):
         import torch

@@ -23,9 +23,6 @@
 // requantises it in a separate pass).  FC2: fp32 y rows in route-row order.
 #include "moe_internal.h"
 
-#ifndef MOE_KSPLIT4_KB
-#define MOE_KSPLIT4_KB 32
-#endif
 // Weight loads with the non-temporal hint: bit 0 for FC1, bit 1 for FC2.
 #ifndef MOE_NT_LOADS
 #define MOE_NT_LOADS 1
@@ -213,10 +210,10 @@ struct Sched {};
 
 template <bool FC1, bool MX, int NBW, int P>
 hipError_t launch_sched(Sched<NBW, P>, const FcArgs& a, int tiles_max, hipStream_t stream) {
-  // K split: four ranges for long K (>= MOE_KSPLIT4_KB column blocks), two
+  // K split: four ranges for long K (>= kKsplit4Blocks column blocks), two
   // otherwise.  It depends on K alone, so every batch size sums a row in the
   // same order.
-  if (a.mat.kb >= MOE_KSPLIT4_KB) return launch_dec<FC1, MX, NBW, 4, P>(a, tiles_max, stream);
+  if (a.mat.kb >= kKsplit4Blocks) return launch_dec<FC1, MX, NBW, 4, P>(a, tiles_max, stream);
   return launch_dec<FC1, MX, NBW, 2, P>(a, tiles_max, stream);
 }
 

@@ -11,6 +11,8 @@
 
 #include <cstdarg>
 #include <cstdio>
+#include <atomic>
+#include <cstdlib>
 #include <cstring>
 #include <string>
 
@@ -108,6 +110,7 @@ Layout make_layout(int H, int I, int E, int k, int Tmax, int act) {
     L.ws_h = o; o = align_up(o + 2 * R * I, A);
   }
   L.ws_y = o; o = align_up(o + 4 * R * H, A);
+  L.ws_sync = o; o = align_up(o + kFusedSyncBytes, A);
   L.ws_bytes = o;
   return L;
 }
@@ -120,6 +123,7 @@ struct moe_mxfp4_plan_s {
   const uint8_t* repacked;
   hipEvent_t events[5];
   int n_events;
+  uint32_t fused_gen;   // generation of this plan's last fused forward (0: none)
 };
 
 namespace {
@@ -209,6 +213,7 @@ moe_status moe_mxfp4_plan(const moe_mxfp4_config* cfg, const uint8_t* w13_codes,
   p->L = L;
   p->repacked = rp;
   p->n_events = 0;
+  p->fused_gen = 0;
   *out = p;
   return ok();
 }
@@ -221,9 +226,43 @@ static moe_status check_ws(const moe_mxfp4_plan_s* p, void* workspace, size_t wo
   return MOE_OK;
 }
 
-moe_status moe_mxfp4_forward(moe_mxfp4_plan_t p, const uint16_t* hidden, const int32_t* topk_ids,
-                             const float* topk_weights, int32_t T, float* acc_fp32, uint16_t* out_bf16,
-                             void* workspace, size_t workspace_bytes, hipStream_t stream) {
+// The FC1 and FC2 arguments of one forward: weights, route outputs, the
+// activations each reads and the workspace rows each writes.
+static void fc_args(const moe_mxfp4_plan_s* p, uint8_t* ws, const moe::RouteOut& ro, const uint16_t* hidden,
+                    int32_t T, moe::FcArgs* f1, moe::FcArgs* f2) {
+  const moe::Layout& L = p->L;
+  const bool mx = p->cfg.act == MOE_ACT_MXFP8;
+  *f1 = moe::FcArgs{};
+  f1->codes = p->repacked + L.rp_w13_codes;
+  f1->scales = p->repacked + L.rp_w13_scales;
+  f1->mat = L.w13;
+  f1->tiles = ro.tiles;
+  f1->tile_count = ro.tile_count;
+  f1->offsets = ro.offsets;
+  f1->perm = ro.perm;
+  f1->top_k = L.k;
+  f1->a = mx ? static_cast<const void*>(ws + L.ws_xq) : static_cast<const void*>(hidden);
+  f1->a_scales = mx ? ws + L.ws_xs : nullptr;
+  f1->lda = L.H;
+  f1->a_rows = T;
+  f1->out = ws + L.ws_h;
+  f1->ldo = L.I;
+  *f2 = *f1;
+  f2->codes = p->repacked + L.rp_w2_codes;
+  f2->scales = p->repacked + L.rp_w2_scales;
+  f2->mat = L.w2;
+  f2->a = mx ? static_cast<const void*>(ws + L.ws_hq) : static_cast<const void*>(ws + L.ws_h);
+  f2->a_scales = mx ? ws + L.ws_hs : nullptr;
+  f2->lda = L.I;
+  f2->a_rows = T * L.k;
+  f2->out = ws + L.ws_y;
+  f2->ldo = L.H;
+}
+
+// The argument checks every forward entry makes.
+static moe_status check_forward(moe_mxfp4_plan_t p, const uint16_t* hidden, const int32_t* topk_ids,
+                                const float* topk_weights, int32_t T, float* acc_fp32, uint16_t* out_bf16,
+                                void* workspace, size_t workspace_bytes) {
   if (!p) return fail(MOE_ERR_ARG, "plan is null");
   if (T < 0) return fail(MOE_ERR_ARG, "num_tokens must be >= 0, got %d", T);
   if (T > p->cfg.max_tokens)
@@ -237,6 +276,15 @@ moe_status moe_mxfp4_forward(moe_mxfp4_plan_t p, const uint16_t* hidden, const i
   }
   if (acc_fp32 && misaligned(acc_fp32))
     return fail(MOE_ERR_ALIGN, "acc_fp32 must be 16-byte aligned, got %p", (void*)acc_fp32);
+  return MOE_OK;
+}
+
+moe_status moe_mxfp4_forward(moe_mxfp4_plan_t p, const uint16_t* hidden, const int32_t* topk_ids,
+                             const float* topk_weights, int32_t T, float* acc_fp32, uint16_t* out_bf16,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (moe_status s = check_forward(p, hidden, topk_ids, topk_weights, T, acc_fp32, out_bf16, workspace,
+                                   workspace_bytes))
+    return s;
   if (T == 0) return ok();
 
   const moe::Layout& L = p->L;
@@ -271,21 +319,8 @@ moe_status moe_mxfp4_forward(moe_mxfp4_plan_t p, const uint16_t* hidden, const i
   if (mx) CHK(moe::launch_quant_bf16(hidden, T, L.H, ws + L.ws_xq, ws + L.ws_xs, stream), "x quant launch");
   REC(1);
 
-  moe::FcArgs f1{};
-  f1.codes = p->repacked + L.rp_w13_codes;
-  f1.scales = p->repacked + L.rp_w13_scales;
-  f1.mat = L.w13;
-  f1.tiles = ro.tiles;
-  f1.tile_count = ro.tile_count;
-  f1.offsets = ro.offsets;
-  f1.perm = ro.perm;
-  f1.top_k = L.k;
-  f1.a = mx ? static_cast<const void*>(ws + L.ws_xq) : static_cast<const void*>(hidden);
-  f1.a_scales = mx ? ws + L.ws_xs : nullptr;
-  f1.lda = L.H;
-  f1.a_rows = T;
-  f1.out = ws + L.ws_h;
-  f1.ldo = L.I;
+  moe::FcArgs f1, f2;
+  fc_args(p, ws, ro, hidden, T, &f1, &f2);
   if (prefill) CHK(moe::launch_fc1_prefill(f1, bm, tiles_max, stream), "FC1 launch");
   else if (prefill_mx) CHK(moe::launch_fc1_prefill_mx(f1, tiles_max, stream), "FC1 launch");
   else CHK(mx ? moe::launch_fc1_mx(f1, tiles_max, T, stream) : moe::launch_fc1_bf16(f1, tiles_max, T, stream),
@@ -295,16 +330,6 @@ moe_status moe_mxfp4_forward(moe_mxfp4_plan_t p, const uint16_t* hidden, const i
   if (mx)
     CHK(moe::launch_quant_f32(reinterpret_cast<const float*>(ws + L.ws_h), ro.offsets + L.E, T * L.k, L.I,
                               ws + L.ws_hq, ws + L.ws_hs, stream), "h quant launch");
-  moe::FcArgs f2 = f1;
-  f2.codes = p->repacked + L.rp_w2_codes;
-  f2.scales = p->repacked + L.rp_w2_scales;
-  f2.mat = L.w2;
-  f2.a = mx ? static_cast<const void*>(ws + L.ws_hq) : static_cast<const void*>(ws + L.ws_h);
-  f2.a_scales = mx ? ws + L.ws_hs : nullptr;
-  f2.lda = L.I;
-  f2.a_rows = R;
-  f2.out = ws + L.ws_y;
-  f2.ldo = L.H;
   if (prefill) CHK(moe::launch_fc2_prefill(f2, bm, tiles_max, stream), "FC2 launch");
   else if (prefill_mx) CHK(moe::launch_fc2_prefill_mx(f2, tiles_max, stream), "FC2 launch");
   else CHK(mx ? moe::launch_fc2_mx(f2, tiles_max, T, stream) : moe::launch_fc2_bf16(f2, tiles_max, T, stream),
@@ -316,6 +341,59 @@ moe_status moe_mxfp4_forward(moe_mxfp4_plan_t p, const uint16_t* hidden, const i
   REC(4);
 #undef REC
 #undef CHK
+  return ok();
+}
+
+moe_status moe_mxfp4_forward_fused(moe_mxfp4_plan_t p, const uint16_t* hidden, const int32_t* topk_ids,
+                                   const float* topk_weights, int32_t T, float* acc_fp32, uint16_t* out_bf16,
+                                   void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (moe_status s = check_forward(p, hidden, topk_ids, topk_weights, T, acc_fp32, out_bf16, workspace,
+                                   workspace_bytes))
+    return s;
+  const moe::Layout& L = p->L;
+  if (p->cfg.act != MOE_ACT_BF16)
+    return fail(MOE_ERR_SHAPE, "the fused forward takes MOE_ACT_BF16 plans, got act=%d", p->cfg.act);
+  if ((int64_t)T * L.k > moe::kFusedMaxRoutes)
+    return fail(MOE_ERR_SHAPE, "the fused forward takes at most %d routes (num_tokens*top_k), got %lld",
+                moe::kFusedMaxRoutes, (long long)T * L.k);
+  if (T == 0) return ok();
+  // a process-wide generation: the error word of an earlier forward, of any
+  // plan, never matches this one
+  static std::atomic<uint32_t> generation{0};
+  uint32_t gen;
+  do gen = generation.fetch_add(1) + 1;
+  while (gen == 0);
+  long long spin = 10000000;   // 100 ms of the 100 MHz s_memrealtime clock per wait
+  if (const char* env = std::getenv("MOE_FUSED_SPIN_TICKS")) spin = std::atoll(env);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  const moe::RouteOut ro = route_out(L, ws);
+  moe::FcArgs f1, f2;
+  fc_args(p, ws, ro, hidden, T, &f1, &f2);
+  hipError_t e;
+  if (p->n_events > 0 && (e = hipEventRecord(p->events[0], stream)) != hipSuccess)
+    return hip_fail(e, "hipEventRecord");
+  if ((e = moe::launch_fused_decode(f1, f2, topk_ids, topk_weights, T, L.k, L.E, L.H, acc_fp32, out_bf16, ro,
+                                    ws + L.ws_sync, gen, spin, stream)) != hipSuccess)
+    return hip_fail(e, "fused decode launch");
+  for (int i = 1; i < p->n_events; ++i)   // one kernel: every later stage boundary is its end
+    if ((e = hipEventRecord(p->events[i], stream)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+  p->fused_gen = gen;
+  return ok();
+}
+
+moe_status moe_mxfp4_fused_status(moe_mxfp4_plan_t p, void* workspace, size_t workspace_bytes,
+                                  hipStream_t stream) {
+  if (!p) return fail(MOE_ERR_ARG, "plan is null");
+  if (moe_status s = check_ws(p, workspace, workspace_bytes)) return s;
+  if (p->fused_gen == 0) return ok();
+  hipError_t e;
+  if ((e = hipStreamSynchronize(stream)) != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+  uint32_t word = 0;
+  const uint8_t* err = static_cast<const uint8_t*>(workspace) + p->L.ws_sync + 4 * (2 * (size_t)moe::kFusedMaxTiles + 1);
+  if ((e = hipMemcpy(&word, err, 4, hipMemcpyDeviceToHost)) != hipSuccess) return hip_fail(e, "hipMemcpy");
+  if (word == p->fused_gen)
+    return fail(MOE_ERR_TIMEOUT, "a wait of the last fused forward (generation %u) passed its time bound; "
+                "its outputs are not valid", word);
   return ok();
 }
 

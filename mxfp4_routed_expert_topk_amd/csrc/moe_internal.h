@@ -30,6 +30,10 @@ constexpr int kTileBytes = 1024;    // codes per tile
 constexpr int kScaleGroupBytes = 256;
 constexpr int kRouteChunk = 1024;   // routes per route workgroup
 constexpr int kBM = 16;             // rows per FC tile (one MFMA M block)
+// K column blocks from which the decode kernels split K four ways (else two):
+// a function of K alone, so a row's fp32 summation order depends neither on
+// the batch nor on the kernel (the fused decode kernel uses the same split).
+constexpr int kKsplit4Blocks = 32;
 constexpr int kMaxDimension = 16384;  // largest hidden / intermediate size a plan accepts
 
 struct MatLayout {
@@ -59,7 +63,7 @@ struct Layout {
   size_t rp_w13_codes, rp_w13_scales, rp_w2_codes, rp_w2_scales, rp_status, rp_bytes;
   // workspace
   size_t ws_counts, ws_offsets, ws_perm, ws_rowpos, ws_tiles, ws_tile_count, ws_blockcounts;
-  size_t ws_xq, ws_xs, ws_h, ws_hq, ws_hs, ws_y, ws_bytes;
+  size_t ws_xq, ws_xs, ws_h, ws_hq, ws_hs, ws_y, ws_sync, ws_bytes;
 };
 
 Layout make_layout(int H, int I, int E, int k, int Tmax, int act);
@@ -119,6 +123,17 @@ hipError_t launch_fc2_prefill(const FcArgs& a, int bm, int tiles_max, hipStream_
 constexpr int kPrefillMxRows = 128;
 hipError_t launch_fc1_prefill_mx(const FcArgs& a, int tiles_max, hipStream_t stream);
 hipError_t launch_fc2_prefill_mx(const FcArgs& a, int tiles_max, hipStream_t stream);
+
+// The whole bf16 decode layer in one cooperative launch (fused.hip), for at
+// most kFusedMaxRoutes routes.  `sync` is kFusedSyncBytes of workspace, zero
+// before its first use (the kernel keeps it consistent afterwards).
+constexpr int kFusedMaxRoutes = 256;
+constexpr int kFusedMaxTiles = kFusedMaxRoutes / kBM + kFusedMaxRoutes;   // tile list bound, any E
+constexpr size_t kFusedSyncBytes = 4 * (2 * (size_t)kFusedMaxTiles + 2);   // two counts per tile, two words
+hipError_t launch_fused_decode(const FcArgs& f1, const FcArgs& f2, const int32_t* ids, const float* weights,
+                               int32_t T, int32_t k, int32_t E, int32_t H, float* acc, uint16_t* out,
+                               const RouteOut& route, uint8_t* sync, uint32_t gen, long long spin_ticks,
+                               hipStream_t stream);
 
 // Router top-k (E <= kRouterMaxExperts, k <= 32).
 constexpr int kRouterMaxExperts = 1024;

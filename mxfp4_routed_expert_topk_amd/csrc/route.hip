@@ -13,7 +13,7 @@
 // Decode-sized problems (T*k <= 256) run in one wave, mid-sized ones
 // (<= 1024) as one workgroup; larger ones as count -> scan -> scatter over
 // 1024-route chunks.
-#include "moe_internal.h"
+#include "route_wave.h"
 
 namespace moe {
 namespace {
@@ -46,20 +46,6 @@ __device__ int block_inclusive_scan(int v, int* tmp) {
   int r = v + (w > 0 ? tmp[w - 1] : 0);
   __syncthreads();
   return r;
-}
-
-// Mask of the lanes of this wave that hold the same valid expert id.
-__device__ __forceinline__ uint64_t match_expert(int e, bool valid) {
-  uint64_t todo = __ballot(valid);
-  uint64_t mine = 0;
-  while (todo) {
-    const int leader = __ffsll((unsigned long long)todo) - 1;
-    const int el = __builtin_amdgcn_readlane(e, leader);
-    const uint64_t m = __ballot(valid && e == el);
-    if (valid && e == el) mine = m;
-    todo &= ~m;
-  }
-  return mine;
 }
 
 // Counts per expert, offsets, tile list.  `cnt` is the per-expert total
@@ -129,74 +115,12 @@ __global__ __launch_bounds__(kThreads) void route_fused(const int32_t* ids, int 
   scatter_chunk(ids, R, E, 0, s_off, wcnt, o);
 }
 
-// One wave: everything for R <= kSmallRoutes (decode batches).  No workgroup
-// barriers: lane l holds routes l, l+64, ... in f order; a 64-route chunk at
-// a time gets its ranks from ballots (match_expert), plus a running per-expert
-// count in LDS that one lane per expert advances after the chunk -- the same
-// (expert, f) order as the chunked kernels.
-constexpr int kSmallRoutes = 256;
+constexpr int kSmallRoutes = 256;   // routes the one-wave kernel takes (route_wave.h)
 
+// One wave: everything for R <= kSmallRoutes (decode batches).
 __global__ __launch_bounds__(kWave) void route_small(const int32_t* ids, int R, int E, int bm, RouteOut o) {
   __shared__ int s_cnt[1024];    // per-expert count, then running row position
-  const int lane = threadIdx.x;
-  for (int e = lane; e < E; e += kWave) s_cnt[e] = 0;
-  __syncthreads();   // one wave: orders the LDS accesses (compiler and hardware)
-  for (int f = lane; f < R; f += kWave) {
-    const int e = ids[f];
-    if (e >= 0 && e < E) atomicAdd(&s_cnt[e], 1);
-  }
-  __syncthreads();
-  // exclusive scans of the counts and of the tile counts, 16 experts per lane
-  // step (ascending expert order; one wave, so lane order is the scan order)
-  int run = 0, trun = 0;
-  for (int base = 0; base < E; base += kWave) {
-    const int e = base + lane;
-    const int c = e < E ? s_cnt[e] : 0;
-    const int nt = (c + bm - 1) / bm;
-    int incl = c, tincl = nt;
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-      const int t1 = __shfl_up(incl, d, kWave), t2 = __shfl_up(tincl, d, kWave);
-      if (lane >= d) {
-        incl += t1;
-        tincl += t2;
-      }
-    }
-    const int off = run + incl - c, toff = trun + tincl - nt;
-    if (e < E) {
-      o.counts[e] = c;
-      o.offsets[e] = off;
-      for (int i = 0; i < nt; ++i) o.tiles[toff + i] = make_int2(e, off + i * bm);
-      s_cnt[e] = off;   // running row position from here on
-    }
-    run += __shfl(incl, kWave - 1, kWave);
-    trun += __shfl(tincl, kWave - 1, kWave);
-  }
-  if (lane == 0) {
-    o.offsets[E] = run;
-    *o.tile_count = trun;
-  }
-  __syncthreads();
-  // rows: chunk by chunk in f order
-  const uint64_t below = lane ? (~0ull >> (kWave - lane)) : 0ull;
-  for (int base = 0; base < R; base += kWave) {
-    const int f = base + lane;
-    const int e = f < R ? ids[f] : -1;
-    const bool valid = f < R && e >= 0 && e < E;
-    const uint64_t mine = match_expert(e, valid);
-    if (f < R) {
-      if (valid) {
-        const int pos = s_cnt[e] + __popcll(mine & below);
-        o.perm[pos] = f;
-        o.rowpos[f] = pos;
-      } else {
-        o.rowpos[f] = -1;
-      }
-    }
-    __syncthreads();   // every lane has read s_cnt before the leaders advance it
-    if (valid && __popcll(mine & below) == 0) s_cnt[e] += __popcll(mine);
-    __syncthreads();
-  }
+  route_wave(ids, R, E, bm, o, s_cnt);
 }
 
 // Chunked: per-chunk counts.

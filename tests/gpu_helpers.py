@@ -39,7 +39,7 @@ def make_plan(case: W.Case, max_tokens=None, weights=None):
     return plan, w
 
 
-def run_forward(plan, case: W.Case, with_acc=True, nan_acc=None):
+def run_forward(plan, case: W.Case, with_acc=True, nan_acc=None, fused=False):
     x = to_dev(case.hidden_bits).view(torch.bfloat16)
     ids = to_dev(case.topk_ids)
     wts = to_dev(case.topk_weights)
@@ -49,7 +49,11 @@ def run_forward(plan, case: W.Case, with_acc=True, nan_acc=None):
         fill = float("nan") if (case.nan_accumulator if nan_acc is None else nan_acc) else 0.0
         acc = torch.full((T, H), fill, dtype=torch.float32, device=dev())
     out = torch.full((T, H), float("nan"), dtype=torch.bfloat16, device=dev())
-    plan.forward(x, ids, wts, out=out, acc=acc)
+    if fused:
+        plan.forward_fused(x, ids, wts, out=out, acc=acc)
+        plan.fused_status()   # synchronises; raises if a wait timed out
+    else:
+        plan.forward(x, ids, wts, out=out, acc=acc)
     torch.cuda.synchronize()
     return out, acc
 

@@ -186,6 +186,8 @@ def test_forward_small_full(name, make):
     out, acc = G.run_forward(plan, case, nan_acc=True)
     r = check_layer(case, out, acc, ew=case.experts())
     say(f"  max_ulp={r['max_ulp']:.2f} max_rel_l2={r['max_rel_l2']:.2e}")
+    if case.act == "bf16" and s.tokens * s.top_k <= FUSED_MAX_ROUTES:
+        assert_fused_equal(plan, case, out, acc, ew=case.experts())
 
 
 # ------------------------------------------------------------------ full-size configurations, sampled tokens
@@ -231,6 +233,39 @@ def test_forward_decode(m):
     toks = sampled_tokens(case, 2)
     r = check_layer(case, out, acc, tokens=toks)
     say(f"  tokens {toks}: max_ulp={r['max_ulp']:.2f} max_rel_l2={r['max_rel_l2']:.2e}")
+    if m * case.shape.top_k <= FUSED_MAX_ROUTES:
+        assert_fused_equal(plan, case, out, acc)
+
+
+FUSED_MAX_ROUTES = 256
+
+
+def assert_fused_equal(plan, case, out, acc, tokens=None, ew=None):
+    """The one-launch forward gives the multi-launch forward's outputs bit for bit
+    where that takes the 16-row kernels (the same K split and order); where it
+    takes the 128-row prefill kernels (a different K order) the fused outputs
+    meet the oracle on their own."""
+    s = case.shape
+    R = s.tokens * s.top_k
+    say(f"  fused forward, {R} routes")
+    out2, acc2 = G.run_forward(plan, case, fused=True)
+    if R < 16 * s.experts or s.hidden % 256:
+        np.testing.assert_array_equal(G.bf16_bits(out2), G.bf16_bits(out))
+        np.testing.assert_array_equal(acc2.cpu().numpy().view(np.uint32), acc.cpu().numpy().view(np.uint32))
+    else:
+        check_layer(case, out2, acc2, tokens=tokens, ew=ew)
+
+
+def test_forward_decode_fused_at_its_limit():
+    """256 routes (32 tokens, top-8): the largest batch the fused forward takes."""
+    case = W.config_case(1, m=32)
+    say("forward decode M=32, fused and multi-launch")
+    plan = big_plan(1, case, max(W.DECODE_M))
+    out, acc = G.run_forward(plan, case)
+    assert_fused_equal(plan, case, out, acc)
+    toks = sampled_tokens(case, 3)
+    r = check_layer(case, out, acc, tokens=toks)
+    say(f"  tokens {toks}: max_ulp={r['max_ulp']:.2f} max_rel_l2={r['max_rel_l2']:.2e}")
 
 
 @pytest.mark.parametrize("cid", [2, 3, 4])
@@ -266,6 +301,8 @@ def test_forward_k3_shapes(m, act):
     out, acc = G.run_forward(_plans[key], case)
     assert torch.isfinite(acc).all()
     np.testing.assert_array_equal(G.bf16_bits(out), oracle.f32_to_bf16_rne(acc.cpu().numpy()))
+    if act == "bf16" and m * case.shape.top_k <= FUSED_MAX_ROUTES:
+        assert_fused_equal(_plans[key], case, out, acc)
     toks = sampled_tokens(case, 3)
     r = check_layer(case, out, acc, tokens=toks)
     say(f"  tokens {toks}: max_ulp={r['max_ulp']:.2f} max_rel_l2={r['max_rel_l2']:.2e}")
@@ -412,6 +449,86 @@ def test_errors_are_reported(mid):
     plan.forward(x, ids, wts, out=out, num_tokens=0)
     torch.cuda.synchronize()
     assert (out == 7.0).all()
+
+
+# ------------------------------------------------------------------ the one-launch (fused) decode forward
+def _fused_checked(plan, case, **kw):
+    """Run a case both ways; the fused outputs must equal the multi-launch ones bit
+    for bit where those come from the 16-row kernels, else meet the oracle.
+    Returns the fused (out bits, acc)."""
+    import dataclasses
+    c = dataclasses.replace(case, **kw)
+    out, acc = G.run_forward(plan, c, nan_acc=True)
+    assert_fused_equal(plan, c, out, acc)
+    out2, acc2 = G.run_forward(plan, c, nan_acc=True, fused=True)
+    return G.bf16_bits(out2), acc2.cpu().numpy()
+
+
+def test_fused_calls_in_sequence_on_one_workspace(mid):
+    """Fused and multi-launch calls alternate on one workspace, with other routes and
+    other token counts each time (40 and 33 tokens put the multi-launch forward on
+    the prefill kernels, 7 and 1 on the 16-row ones)."""
+    import dataclasses
+    case, plan, _ = mid
+    say("fused: calls in sequence")
+    rng = np.random.default_rng(7)
+    for T in (40, 7, 1, 33):
+        ids = rng.integers(-1, 8, size=(T, case.shape.top_k)).astype(np.int32)
+        _fused_checked(plan, case, topk_ids=ids, topk_weights=case.topk_weights[:T].copy(),
+                       hidden_bits=case.hidden_bits[:T].copy(), shape=dataclasses.replace(case.shape, tokens=T))
+
+
+def test_fused_edge_cases(mid):
+    case, plan, _ = mid
+    say("fused: no valid route, duplicate ids, no tokens")
+    none = np.full_like(case.topk_ids, -1)
+    none[::2] = 7   # ids 6, 7 are not resident (E = 6)
+    out, acc = _fused_checked(plan, case, topk_ids=none)
+    assert not out.any() and not acc.view(np.uint32).any()   # +0 everywhere, the NaN fill overwritten
+    _fused_checked(plan, case, topk_ids=np.repeat(case.topk_ids[:, :1], 3, axis=1))
+    x = G.to_dev(case.hidden_bits).view(torch.bfloat16)
+    out = torch.full((1, 512), 7.0, dtype=torch.bfloat16, device=x.device)
+    plan.forward_fused(x, G.to_dev(case.topk_ids), G.to_dev(case.topk_weights), out=out, num_tokens=0)
+    torch.cuda.synchronize()
+    assert (out == 7.0).all()
+
+
+def test_fused_rejects_what_it_does_not_take():
+    say("fused: MXFP8 plans and more than 256 routes are refused")
+    case = W.make_case("fused_big", W.LayerShape(90, 256, 128, 4, 4, 3), 47)
+    plan, _ = G.make_plan(case)
+    x = G.to_dev(case.hidden_bits).view(torch.bfloat16)
+    ids, wts = G.to_dev(case.topk_ids), G.to_dev(case.topk_weights)
+    with pytest.raises(moe.MoeError) as ei:
+        plan.forward_fused(x, ids, wts)                      # 270 routes
+    assert ei.value.status == 2 and "at most 256 routes" in ei.value.message
+    plan.forward_fused(x, ids, wts, num_tokens=85)           # 255 routes: taken
+    plan.fused_status()
+    mx = W.make_case("fused_mx", W.LayerShape(4, 256, 128, 4, 4, 2), 48, act="mxfp8")
+    mplan, _ = G.make_plan(mx)
+    with pytest.raises(moe.MoeError) as ei:
+        mplan.forward_fused(G.to_dev(mx.hidden_bits).view(torch.bfloat16), G.to_dev(mx.topk_ids),
+                            G.to_dev(mx.topk_weights))
+    assert ei.value.status == 2 and "MOE_ACT_BF16" in ei.value.message
+
+
+def test_fused_wait_bound_is_reported_and_leaves_later_calls_intact(mid, monkeypatch):
+    """A negative time bound makes every wait that does not find its count at
+    once give up: the kernel still ends, and the status says whether any did.
+    The next call, with the normal bound, is exact again."""
+    case, plan, _ = mid
+    say("fused: the wait bound")
+    ref_out, ref_acc = _fused_checked(plan, case)
+    monkeypatch.setenv("MOE_FUSED_SPIN_TICKS", "-1")
+    try:
+        out, acc = G.run_forward(plan, case, nan_acc=True, fused=True)
+        np.testing.assert_array_equal(G.bf16_bits(out), ref_out)   # no wait gave up this time
+    except moe.MoeError as err:
+        assert err.status == 9 and "time bound" in err.message
+    monkeypatch.delenv("MOE_FUSED_SPIN_TICKS")
+    out, acc = G.run_forward(plan, case, nan_acc=True, fused=True)
+    np.testing.assert_array_equal(G.bf16_bits(out), ref_out)
+    np.testing.assert_array_equal(acc.cpu().numpy().view(np.uint32), ref_acc.view(np.uint32))
 
 
 @pytest.mark.parametrize("byte,act,bad", [(0xFF, "bf16", True), (0x00, "mxfp8", True), (0x01, "bf16", True),

@@ -95,6 +95,9 @@ def test_forward_and_route_reject_null_plan(lib):
     assert b"plan is null" in lib.moe_mxfp4_last_error()
     assert lib.moe_mxfp4_route(None, 16, 1, 16, 16, 16, 16, 16, 1, None) == 1
     assert lib.moe_mxfp4_set_stage_events(None, None, 0) == 1
+    assert lib.moe_mxfp4_forward_fused(None, 16, 16, 16, 1, None, 16, 16, 1, None) == 1
+    assert b"plan is null" in lib.moe_mxfp4_last_error()
+    assert lib.moe_mxfp4_fused_status(None, 16, 1, None) == 1
 
 
 def test_quantize_argument_errors(lib):
