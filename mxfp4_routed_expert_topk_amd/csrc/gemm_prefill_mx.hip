@@ -37,8 +37,8 @@
 // each block one MFMA step, whatever the tile height.
 //
 // FC1: row blocks come in (gate j, up j) pairs (interleaved repack); the
-// epilogue stores h = silu(g) * u in fp32 for the MXFP8 requantisation.  FC2:
-// fp32 y rows in route-row order.
+// epilogue requantises h = silu(g) * u to MXFP8 (E4M3 codes, one E8M0 per 32
+// columns), which FC2 reads.  FC2: fp32 y rows in route-row order.
 #include <type_traits>
 
 #include "moe_internal.h"
@@ -272,6 +272,36 @@ __device__ __forceinline__ void tile_body(const FcArgs& a, uint8_t* sa, int e, i
   MOE_WAIT_VM_LGKM(0);
 
   // ---- epilogue.  16x16 D layout: lane holds column l%16, rows 4(l/16) + i.
+  if constexpr (FC1) {
+    // h = silu(g) * u, requantised to MXFP8 here: the wave's two gate/up pairs
+    // are h columns 16 (nb0/2) + [0, 32), one whole 32-element scale block
+    // (nb0 is a multiple of 4), held by the 16 lanes of a row (column rl and
+    // 16 + rl).  Its amax is reduced over those lanes; every lane shuffles, so
+    // the stores alone are guarded by the row count.
+    static_assert(kNBW == 4, "one 32-column scale block of h per wave");
+    const int hc = (nb0 / 2) * kTileN;   // first h column of the block
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * mb + 4 * q + i;
+        const float h0 = silu_f32(acc[mb][0][i]) * acc[mb][1][i];
+        const float h1 = silu_f32(acc[mb][2][i]) * acc[mb][3][i];
+        float m = fmaxf(fabsf(h0), fabsf(h1));
+#pragma unroll
+        for (int d = 1; d < 16; d <<= 1) m = fmaxf(m, __shfl_xor(m, d, kWave));
+        const int ex = mx_scale_exp(m);
+        const float inv = __uint_as_float((uint32_t)(127 - ex) << 23);   // 2^-e
+        if (r < rows) {
+          uint8_t* crow = a.out_codes + (size_t)(row0 + r) * a.ldo + hc;
+          crow[rl] = (uint8_t)e4m3_rne(h0 * inv);
+          crow[16 + rl] = (uint8_t)e4m3_rne(h1 * inv);
+          if (rl == 0) a.out_scales[(size_t)(row0 + r) * (a.ldo / 32) + hc / 32] = (uint8_t)(ex + 127);
+        }
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
@@ -279,11 +309,7 @@ __device__ __forceinline__ void tile_body(const FcArgs& a, uint8_t* sa, int e, i
       const int r = 16 * mb + 4 * q + i;
       if (r >= rows) continue;
       float* orow = static_cast<float*>(a.out) + (size_t)(row0 + r) * a.ldo;
-      if constexpr (FC1) {
-#pragma unroll
-        for (int j = 0; j < kNBW / 2; ++j)   // row blocks 2j, 2j+1: gate and up of pair nb0/2 + j
-          orow[(size_t)(nb0 / 2 + j) * kTileN + rl] = silu_f32(acc[mb][2 * j][i]) * acc[mb][2 * j + 1][i];
-      } else {
+      {
 #pragma unroll
         for (int j = 0; j < kNBW; ++j) orow[(size_t)(nb0 + j) * kTileN + rl] = acc[mb][j][i];
       }

@@ -247,6 +247,8 @@ static void fc_args(const moe_mxfp4_plan_s* p, uint8_t* ws, const moe::RouteOut&
   f1->a_rows = T;
   f1->out = ws + L.ws_h;
   f1->ldo = L.I;
+  f1->out_codes = mx ? ws + L.ws_hq : nullptr;
+  f1->out_scales = mx ? ws + L.ws_hs : nullptr;
   *f2 = *f1;
   f2->codes = p->repacked + L.rp_w2_codes;
   f2->scales = p->repacked + L.rp_w2_scales;
@@ -327,7 +329,7 @@ moe_status moe_mxfp4_forward(moe_mxfp4_plan_t p, const uint16_t* hidden, const i
            "FC1 launch");
   REC(2);
 
-  if (mx)
+  if (mx && !prefill_mx)   // the MXFP8 prefill FC1 requantises h itself
     CHK(moe::launch_quant_f32(reinterpret_cast<const float*>(ws + L.ws_h), ro.offsets + L.E, T * L.k, L.I,
                               ws + L.ws_hq, ws + L.ws_hs, stream), "h quant launch");
   if (prefill) CHK(moe::launch_fc2_prefill(f2, bm, tiles_max, stream), "FC2 launch");

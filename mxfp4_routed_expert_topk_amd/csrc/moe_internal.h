@@ -106,6 +106,8 @@ struct FcArgs {
   int32_t a_rows;           // rows of A (FC1: tokens; FC2: routes)
   void* out;                // FC1: h ([R,I] bf16, or fp32 for MXFP8); FC2: y [R,H] fp32
   int32_t ldo;              // elements per output row
+  uint8_t* out_codes;       // MXFP8 prefill FC1: h as E4M3 codes [R,I] (instead of fp32 `out`)
+  uint8_t* out_scales;      // ... and its E8M0 bytes [R,I/32]
 };
 // `tokens` (the batch size) only picks a schedule; results do not depend on it.
 hipError_t launch_fc1_bf16(const FcArgs& a, int tiles_max, int tokens, hipStream_t stream);
@@ -119,7 +121,9 @@ int prefill_rows(int tokens, int top_k, int experts);
 hipError_t launch_fc1_prefill(const FcArgs& a, int bm, int tiles_max, hipStream_t stream);
 hipError_t launch_fc2_prefill(const FcArgs& a, int bm, int tiles_max, hipStream_t stream);
 // Prefill FC kernels of the MXFP8 path over 128-row tiles (needs N % 256 == 0
-// and A plus its scales addressable with 32-bit offsets).
+// and A plus its scales addressable with 32-bit offsets).  FC1 writes h already
+// requantised to MXFP8 (out_codes / out_scales) by the rule launch_quant_f32
+// applies to an fp32 h.
 constexpr int kPrefillMxRows = 128;
 hipError_t launch_fc1_prefill_mx(const FcArgs& a, int tiles_max, hipStream_t stream);
 hipError_t launch_fc2_prefill_mx(const FcArgs& a, int tiles_max, hipStream_t stream);
@@ -177,6 +181,35 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 }
 
 __device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + __expf(-z)); }
+
+// MXFP8 scale rule of the MXFP8 x MXFP4 workload: e = floor(log2(amax / 448)),
+// clamped to [-127, 127], amax = 0 -> -127; the block is scaled by 2^-e,
+// saturated to +-448 and rounded to nearest even E4M3FN (subnormals included);
+// the scale byte is e + 127.  Integer and power-of-two arithmetic on the fp32
+// value only, so the codes do not depend on a hardware converter.
+// floor(log2(amax / 448)) for finite amax >= 0, clamped to [-127, 127].
+__device__ __forceinline__ int mx_scale_exp(float amax) {
+  const uint32_t u = __float_as_uint(amax);
+  const int ex = (int)((u >> 23) & 0xFFu);
+  if (ex == 0) return -127;                      // zero or subnormal: far below 448 * 2^-127
+  const uint32_t man = u & 0x7FFFFFu;
+  int e = (ex - 127) - 8 - (man < 0x600000u ? 1 : 0);   // 448 = 1.75 * 2^8
+  return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
+// |a| already scaled; saturate to 448 and round to nearest even E4M3FN,
+// without branches.  Normal range (a >= 2^-6): round the fp32 mantissa to
+// three bits by adding 0x7FFFF plus the lowest kept bit (a carry moves into the
+// exponent), then rebias the exponent from 127 to 7.  Below 2^-6 the step is
+// 2^-9, so the code is a * 512 rounded to nearest even (exact scaling).
+__device__ __forceinline__ uint32_t e4m3_rne(float v) {
+  const uint32_t sign = (__float_as_uint(v) >> 31) << 7;
+  const float a = fminf(fabsf(v), 448.0f);
+  const uint32_t u = __float_as_uint(a);
+  const uint32_t norm = ((u + 0x7FFFFu + ((u >> 20) & 1u)) >> 20) - (120u << 3);
+  const uint32_t sub = (uint32_t)__builtin_rintf(a * 512.0f);
+  return (a < 0.015625f ? sub : norm) | sign;
+}
 #endif
 
 }  // namespace moe

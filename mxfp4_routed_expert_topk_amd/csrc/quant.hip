@@ -3,49 +3,14 @@
 // e4m3 activation quant"; commit 53edfa98: per-token-group FP8 quant of the
 // gathered rows and requant of h before W2, with UE8M0 scales).
 //
-// Scale rule of the MXFP8 x MXFP4 workload: e = floor(log2(amax / 448)),
-// clamped to [-127, 127], amax = 0 -> -127; the block is scaled by 2^-e,
-// saturated to +-448 and rounded to nearest even (subnormals included); the
-// scale byte is e + 127.  With this rule the block maximum lands in
-// [448, 896) and saturates.  Everything is integer or exact power-of-two
-// arithmetic on the fp32 value, so bf16 inputs give codes that do not depend
-// on the hardware converter.
+// Scale rule: mx_scale_exp / e4m3_rne (moe_internal.h).  With it the block
+// maximum lands in [448, 896) and saturates.
 #include "moe_internal.h"
 
 namespace moe {
 namespace {
 
 constexpr int kThreads = 256;
-
-// floor(log2(amax / 448)) for finite amax >= 0, clamped to [-127, 127].
-__device__ __forceinline__ int mx_scale_exp(float amax) {
-  const uint32_t u = __float_as_uint(amax);
-  const int ex = (int)((u >> 23) & 0xFFu);
-  if (ex == 0) return -127;                      // zero or subnormal: far below 448 * 2^-127
-  const uint32_t man = u & 0x7FFFFFu;
-  int e = (ex - 127) - 8 - (man < 0x600000u ? 1 : 0);   // 448 = 1.75 * 2^8
-  return e < -127 ? -127 : (e > 127 ? 127 : e);
-}
-
-// |a| already scaled; saturate to 448 and round to nearest even E4M3FN.
-__device__ __forceinline__ uint32_t e4m3_rne(float v) {
-  const uint32_t sign = (__float_as_uint(v) >> 31) << 7;
-  float a = fminf(fabsf(v), 448.0f);
-  uint32_t code;
-  if (a < 0.015625f) {                           // below 2^-6: subnormal step 2^-9
-    code = (uint32_t)__builtin_rintf(a * 512.0f);
-  } else {
-    const uint32_t u = __float_as_uint(a);
-    int ee = (int)((u >> 23) & 0xFFu) - 127 + 7;
-    const uint32_t man = u & 0x7FFFFFu;
-    uint32_t r = man >> 20;
-    const uint32_t rem = man & 0xFFFFFu;
-    if (rem > 0x80000u || (rem == 0x80000u && (r & 1u))) ++r;
-    if (r == 8u) { r = 0u; ++ee; }
-    code = ((uint32_t)ee << 3) | r;
-  }
-  return code | sign;
-}
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
