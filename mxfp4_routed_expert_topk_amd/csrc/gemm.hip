@@ -202,7 +202,7 @@ hipError_t launch_dec(const FcArgs& a, int tiles_max, hipStream_t stream) {
 #define MOE_FC2_SMALL 2, 3
 #endif
 #ifndef MOE_FC2_LARGE
-#define MOE_FC2_LARGE 4, 3
+#define MOE_FC2_LARGE 8, 2
 #endif
 
 template <int NBW, int P>
