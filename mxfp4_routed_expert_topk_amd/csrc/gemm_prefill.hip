@@ -41,12 +41,19 @@
 //
 // Work order: the flat list of (tile, column slice) items is cut into eight
 // contiguous chunks, one per XCD (workgroups are dispatched round-robin over
-// the XCDs).  Within it, items run in groups of kTileGroup consecutive tiles
+// the XCDs).  The grid is persistent (as many workgroups as the device holds):
+// a workgroup takes the next item of its XCD's chunk from that chunk's counter
+// and, once the chunk is done, items left in the other chunks.  Under skewed
+// (Zipf) routing the chunks' work differs by tens of percent -- an XCD whose
+// chunk holds the most popular experts' full tiles would otherwise finish
+// last while the others idle.  Within a chunk, items run in groups of kTileGroup consecutive tiles
 // as (group, slice, tile in group): the tiles of a group that belong to one
 // expert -- an expert with many rows has many consecutive tiles -- read the
 // same weight slice at the same time and share it in L2, while the slices of
 // one tile still fall within one XCD's concurrent workgroups and share the
 // tile's activation rows.
+#include <algorithm>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -231,6 +238,20 @@ __device__ __forceinline__ void k_loop(uint8_t* smem, const StageSrc<C>& src, in
   }
 }
 
+template <bool FC1, int BM, int W>
+__device__ __noinline__ void fc_pre_item(const FcArgs& a, uint8_t* smem, int slices, int ntiles, int w,
+                                            int* s_item, int* counter);
+
+// Workgroup barrier for LDS only: this wave's LDS accesses have completed (no
+// wait for its global stores), then s_barrier; the empty asm statements keep
+// the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0) alone
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // W waves side by side: each owns all BM rows x one 64-column group, so every
 // weight fragment is dequantised once per workgroup.  W = 4: two workgroups
 // per CU.  W = 8: 512 columns per workgroup, one per CU -- each staged
@@ -241,21 +262,62 @@ __global__ __launch_bounds__(W * kWave)
 __attribute__((amdgpu_waves_per_eu(Cfg<BM, W>::kWavesPerSimd, Cfg<BM, W>::kWavesPerSimd)))
 void fc_pre(FcArgs a, int slices) {
   using C = Cfg<BM, W>;
-  constexpr int MI = C::MI;
-  constexpr int NJ = 2;                      // 32-column MFMA blocks per wave (its 64 columns)
   __shared__ __align__(1024) uint8_t smem[3 * C::kBytes];
+  __shared__ int s_item;
 
   const int ntiles = *a.tile_count;
   const int total = (ntiles + kTileGroup - 1) / kTileGroup * kTileGroup * slices;   // whole groups
-  const int xcd = blockIdx.x & 7, qq = blockIdx.x >> 3;
-  const int chunk = (total + 7) >> 3;
-  const int w = xcd * chunk + qq;
-  if (qq >= chunk || w >= total) return;
-  // items in groups of kTileGroup consecutive tiles: (group, slice, tile in group)
+  const int chunk = (total + kXcds - 1) / kXcds;
+  const int xcd = blockIdx.x % kXcds;
+  const bool leader = threadIdx.x == 0;
+  // Persistent: take items of this XCD's chunk from its counter, then those
+  // left in the other chunks.  The leader's atomic for the next item goes out
+  // once the current item's K loop is done, so its latency hides under the
+  // epilogue without holding an item back; the result is passed on through
+  // LDS, and the bare barrier at the top of the loop finds every wave done
+  // reading the stage buffers without waiting for the item's output stores.
+  int v = 0, c = xcd;
+  if (leader) s_item = atomicAdd(&a.sched[c], 1);
+  lds_barrier();
+  int i = s_item;
+  for (;;) {
+    const int base = c * chunk, len = min(chunk, total - base);
+    if (i >= len) {                          // chunk c is done: the next one
+      if (++v == kXcds) break;
+      c = (xcd + v) % kXcds;
+      lds_barrier();                         // every wave has read s_item
+      if (leader) s_item = atomicAdd(&a.sched[c], 1);
+      lds_barrier();
+      i = s_item;
+      continue;
+    }
+    fc_pre_item<FC1, BM, W>(a, smem, slices, ntiles, base + i, &s_item, &a.sched[c]);
+    lds_barrier();
+    i = s_item;
+  }
+}
+
+// Item w of the work list: (tile, column slice) in groups of kTileGroup
+// consecutive tiles as (group, slice, tile in group).
+// Kept out of line: inlined into the persistent loop, the item needs more than
+// 256 VGPRs and the spill reloads in its epilogue wait (vmcnt(0)) for every
+// output store already issued.  After the K loop the leader takes the next
+// item from `counter` and, after the epilogue, stores it to *s_item (the K loop's barriers come after every
+// wave's read of *s_item; an empty item takes a barrier of its own).
+template <bool FC1, int BM, int W>
+__device__ __noinline__ void fc_pre_item(const FcArgs& a, uint8_t* smem, int slices, int ntiles, int w,
+                                            int* s_item, int* counter) {
+  using C = Cfg<BM, W>;
+  constexpr int MI = C::MI;
+  constexpr int NJ = 2;                      // 32-column MFMA blocks per wave (its 64 columns)
   const int per_group = kTileGroup * slices;
   const int grp = w / per_group, rem = w - grp * per_group;
   const int slice = rem / kTileGroup, tile = grp * kTileGroup + (rem - slice * kTileGroup);
-  if (tile >= ntiles) return;
+  if (tile >= ntiles) {
+    lds_barrier();   // every wave has read s_item before it is rewritten
+    if (threadIdx.x == 0) *s_item = atomicAdd(counter, 1);
+    return;
+  }
   const int2 td = a.tiles[tile];
   const int e = td.x, row0 = td.y;
   const int rows = min(BM, a.offsets[e + 1] - row0);
@@ -306,6 +368,7 @@ void fc_pre(FcArgs a, int slices) {
       default: k_loop<C, 2>(smem, src, S, wave, lane, acc); break;
     }
   }
+  const int next = threadIdx.x == 0 ? atomicAdd(counter, 1) : 0;
   const int n32 = lane & 31, h = lane >> 5;
 
   // ---- epilogue.  32x32 D layout: lane holds column n32, rows 8(i/4) + 4h + (i%4).
@@ -334,6 +397,7 @@ void fc_pre(FcArgs a, int slices) {
       }
     }
   }
+  if (threadIdx.x == 0) *s_item = next;
 }
 
 #ifndef MOE_PREFILL_WN
@@ -345,7 +409,14 @@ hipError_t launch_cfg(const FcArgs& a, int tiles_max, hipStream_t stream) {
   using C = Cfg<BM, W>;
   const int slices = a.mat.nb / C::kBlocks;
   const long long items = (long long)((tiles_max + kTileGroup - 1) / kTileGroup * kTileGroup) * slices;
-  const long long grid = (items + 7) / 8 * 8;
+  // as many workgroups as the device holds at once (kPerCU per CU), a multiple
+  // of the XCD count, and no more than there can be items
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  const long long resident = (long long)cus * C::kPerCU / kXcds * kXcds;
+  const long long grid = std::max<long long>(kXcds, std::min(resident, (items + kXcds - 1) / kXcds * kXcds));
   hipLaunchKernelGGL((fc_pre<FC1, BM, W>), dim3((unsigned)grid), dim3(W * kWave), 0, stream, a, slices);
   return hipGetLastError();
 }

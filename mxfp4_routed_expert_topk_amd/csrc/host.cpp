@@ -111,6 +111,7 @@ Layout make_layout(int H, int I, int E, int k, int Tmax, int act) {
   }
   L.ws_y = o; o = align_up(o + 4 * R * H, A);
   L.ws_sync = o; o = align_up(o + kFusedSyncBytes, A);
+  L.ws_sched = o; o = align_up(o + 4 * (size_t)kSchedCounters, A);
   L.ws_bytes = o;
   return L;
 }
@@ -137,6 +138,7 @@ moe::RouteOut route_out(const moe::Layout& L, uint8_t* ws) {
   o.tiles = reinterpret_cast<int2*>(ws + L.ws_tiles);
   o.tile_count = reinterpret_cast<int32_t*>(ws + L.ws_tile_count);
   o.blockcounts = reinterpret_cast<int32_t*>(ws + L.ws_blockcounts);
+  o.sched = reinterpret_cast<int32_t*>(ws + L.ws_sched);
   return o;
 }
 
@@ -249,6 +251,7 @@ static void fc_args(const moe_mxfp4_plan_s* p, uint8_t* ws, const moe::RouteOut&
   f1->ldo = L.I;
   f1->out_codes = mx ? ws + L.ws_hq : nullptr;
   f1->out_scales = mx ? ws + L.ws_hs : nullptr;
+  f1->sched = ro.sched;
   *f2 = *f1;
   f2->codes = p->repacked + L.rp_w2_codes;
   f2->scales = p->repacked + L.rp_w2_scales;
@@ -259,6 +262,7 @@ static void fc_args(const moe_mxfp4_plan_s* p, uint8_t* ws, const moe::RouteOut&
   f2->a_rows = T * L.k;
   f2->out = ws + L.ws_y;
   f2->ldo = L.H;
+  f2->sched = ro.sched + moe::kXcds;
 }
 
 // The argument checks every forward entry makes.

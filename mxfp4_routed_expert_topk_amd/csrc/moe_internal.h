@@ -35,6 +35,10 @@ constexpr int kBM = 16;             // rows per FC tile (one MFMA M block)
 // the batch nor on the kernel (the fused decode kernel uses the same split).
 constexpr int kKsplit4Blocks = 32;
 constexpr int kMaxDimension = 16384;  // largest hidden / intermediate size a plan accepts
+// Work counters of the prefill FC kernels: one per XCD chunk of the work list,
+// eight for FC1 then eight for FC2.
+constexpr int kXcds = 8;
+constexpr int kSchedCounters = 2 * kXcds;
 
 struct MatLayout {
   int32_t n, k;        // logical rows / columns
@@ -63,7 +67,7 @@ struct Layout {
   size_t rp_w13_codes, rp_w13_scales, rp_w2_codes, rp_w2_scales, rp_status, rp_bytes;
   // workspace
   size_t ws_counts, ws_offsets, ws_perm, ws_rowpos, ws_tiles, ws_tile_count, ws_blockcounts;
-  size_t ws_xq, ws_xs, ws_h, ws_hq, ws_hs, ws_y, ws_sync, ws_bytes;
+  size_t ws_xq, ws_xs, ws_h, ws_hq, ws_hs, ws_y, ws_sync, ws_sched, ws_bytes;
 };
 
 Layout make_layout(int H, int I, int E, int k, int Tmax, int act);
@@ -82,6 +86,8 @@ struct RouteOut {
   int2* tiles;          // [tiles_max] (expert, first row) of each bm-row FC tile
   int32_t* tile_count;  // [1]
   int32_t* blockcounts; // [route_blocks * E] scratch
+  int32_t* sched;       // [kSchedCounters] work counters of the prefill FC kernels (or null); the
+                        // route kernels zero them, so each forward's FC launches start from zero
 };
 hipError_t launch_route(const Layout& L, const int32_t* ids, int32_t T, const RouteOut& o, int bm,
                         hipStream_t stream);
@@ -108,6 +114,7 @@ struct FcArgs {
   int32_t ldo;              // elements per output row
   uint8_t* out_codes;       // MXFP8 prefill FC1: h as E4M3 codes [R,I] (instead of fp32 `out`)
   uint8_t* out_scales;      // ... and its E8M0 bytes [R,I/32]
+  int32_t* sched;           // bf16 prefill: kXcds work counters of this launch, zero on entry
 };
 // `tokens` (the batch size) only picks a schedule; results do not depend on it.
 hipError_t launch_fc1_bf16(const FcArgs& a, int tiles_max, int tokens, hipStream_t stream);
@@ -116,7 +123,7 @@ hipError_t launch_fc1_mx(const FcArgs& a, int tiles_max, int tokens, hipStream_t
 hipError_t launch_fc2_mx(const FcArgs& a, int tiles_max, int tokens, hipStream_t stream);
 
 // Prefill (MFMA-bound) FC kernels over bm-row tiles, bm in {64, 128}; bf16 path
-// (needs N % 256 == 0).
+// (needs N % 256 == 0).  Persistent: `sched` holds the launch's work counters.
 int prefill_rows(int tokens, int top_k, int experts);
 hipError_t launch_fc1_prefill(const FcArgs& a, int bm, int tiles_max, hipStream_t stream);
 hipError_t launch_fc2_prefill(const FcArgs& a, int bm, int tiles_max, hipStream_t stream);

@@ -102,6 +102,7 @@ __global__ __launch_bounds__(kThreads) void route_fused(const int32_t* ids, int 
   __shared__ int s_off[1024];
   __shared__ int tmp[kWaves];
   __shared__ uint8_t wcnt[kWaves * 1024];
+  if (o.sched != nullptr && threadIdx.x < kSchedCounters) o.sched[threadIdx.x] = 0;
   const int t = threadIdx.x;
   s_cnt[t] = 0;
   __syncthreads();
@@ -120,6 +121,7 @@ constexpr int kSmallRoutes = 256;   // routes the one-wave kernel takes (route_w
 // One wave: everything for R <= kSmallRoutes (decode batches).
 __global__ __launch_bounds__(kWave) void route_small(const int32_t* ids, int R, int E, int bm, RouteOut o) {
   __shared__ int s_cnt[1024];    // per-expert count, then running row position
+  if (o.sched != nullptr && threadIdx.x < kSchedCounters) o.sched[threadIdx.x] = 0;
   route_wave(ids, R, E, bm, o, s_cnt);
 }
 
@@ -141,6 +143,7 @@ __global__ __launch_bounds__(kThreads) void route_count(const int32_t* ids, int 
 // Chunked: totals, offsets, tiles; blockcounts become each chunk's first row per expert.
 __global__ __launch_bounds__(kThreads) void route_scan(int E, int nblk, int bm, RouteOut o) {
   __shared__ int tmp[kWaves];
+  if (o.sched != nullptr && threadIdx.x < kSchedCounters) o.sched[threadIdx.x] = 0;
   const int e = threadIdx.x;
   int total = 0;
   if (e < E)
