@@ -71,10 +71,6 @@ constexpr int kStageA = kRows * kTileK;       // 128 rows x 128 E4M3
 constexpr int kStageBytes = kStageA + kRows * 4;   // + each row's four E8M0 bytes of the stage
 constexpr int kScaleLanes = kRows / kWaves;        // rows whose scale dword one wave copies
 constexpr int kRsrcWord3 = 0x00020000;        // raw buffer, 32-bit data format
-#ifndef MOE_PREFILL_TILE_GROUP
-#define MOE_PREFILL_TILE_GROUP 1
-#endif
-constexpr int kTileGroup = MOE_PREFILL_TILE_GROUP;   // tiles sharing a weight slice in flight
 
 // vmcnt <= n with lgkmcnt 0 (every LDS read of the previous stage returned)
 #define MOE_WAIT_VM_LGKM(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | ((((n) >> 4) & 3) << 14))
@@ -321,17 +317,12 @@ template <bool FC1>
 __global__ __launch_bounds__(kWaves * kWave, 8 / kWaves) void fc_pre_mx(FcArgs a, int slices) {
   __shared__ __align__(1024) uint8_t sa[kBufs * kStageBytes];
   const int ntiles = *a.tile_count;
-  const int total = (ntiles + kTileGroup - 1) / kTileGroup * kTileGroup * slices;   // whole groups
-  // eight contiguous chunks of the (tile, slice) list, one per XCD; within it
-  // groups of kTileGroup tiles of one expert read a weight slice together
-  const int xcd = blockIdx.x & 7, qq = blockIdx.x >> 3;
-  const int chunk = (total + 7) >> 3;
-  const int w = xcd * chunk + qq;
-  if (qq >= chunk || w >= total) return;
-  // items in groups of kTileGroup consecutive tiles: (group, slice, tile in group)
-  const int per_group = kTileGroup * slices;
-  const int grp = w / per_group, rem = w - grp * per_group;
-  const int slice = rem / kTileGroup, tile = grp * kTileGroup + (rem - slice * kTileGroup);
+  // tiles dealt to the XCDs round-robin: XCD x takes tiles x, x + 8, ...,
+  // each with all its column slices in a row, so the slices of a tile share
+  // its activation rows in one L2
+  const int xcd = blockIdx.x % kXcds, qq = blockIdx.x / kXcds;
+  const int q = qq / slices, slice = qq - q * slices;
+  const int tile = xcd + kXcds * q;
   if (tile >= ntiles) return;
   const int2 td = a.tiles[tile];
   const int e = td.x, row0 = td.y;
@@ -347,8 +338,7 @@ __global__ __launch_bounds__(kWaves * kWave, 8 / kWaves) void fc_pre_mx(FcArgs a
 template <bool FC1>
 hipError_t launch(const FcArgs& a, int tiles_max, hipStream_t stream) {
   const int slices = a.mat.nb / kBlocks;
-  const long long items = (long long)((tiles_max + kTileGroup - 1) / kTileGroup * kTileGroup) * slices;
-  const long long grid = (items + 7) / 8 * 8;
+  const long long grid = (long long)(tiles_max + kXcds - 1) / kXcds * slices * kXcds;
   hipLaunchKernelGGL((fc_pre_mx<FC1>), dim3((unsigned)grid), dim3(kWaves * kWave), 0, stream, a, slices);
   return hipGetLastError();
 }
