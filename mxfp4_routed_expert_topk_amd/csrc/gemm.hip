@@ -193,13 +193,13 @@ hipError_t launch_dec(const FcArgs& a, int tiles_max, hipStream_t stream) {
 #define MOE_SMALL_T 16
 #endif
 #ifndef MOE_FC1_SMALL
-#define MOE_FC1_SMALL 2, 3
+#define MOE_FC1_SMALL 2, 2
 #endif
 #ifndef MOE_FC1_LARGE
 #define MOE_FC1_LARGE 4, 2
 #endif
 #ifndef MOE_FC2_SMALL
-#define MOE_FC2_SMALL 2, 3
+#define MOE_FC2_SMALL 2, 2
 #endif
 #ifndef MOE_FC2_LARGE
 #define MOE_FC2_LARGE 8, 2
