@@ -347,6 +347,33 @@ def test_repeat_runs_identical_and_inputs_untouched(mid):
     assert torch.equal(rp, plan.repacked)
 
 
+def test_prefill_workspace_with_stale_bytes_gives_the_same_bits():
+    """The bf16 prefill kernels take their work items from counters in the
+    workspace, which the route stage zeroes in the stream every forward: a
+    workspace full of stale bytes, reused across calls and batch sizes, gives
+    the bits a zeroed workspace gives."""
+    case = W.make_case("stale_ws", W.LayerShape(300, 512, 384, 4, 4, 2), 32, routing="zipf")
+    say("prefill on a workspace of stale bytes")
+    plan, _ = G.make_plan(case)
+    x = G.to_dev(case.hidden_bits).view(torch.bfloat16)
+    ids = G.to_dev(case.topk_ids)
+    wts = G.to_dev(case.topk_weights)
+    ws = torch.full((plan.workspace_bytes,), 0x7F, dtype=torch.uint8, device=x.device)
+
+    def run(n, workspace):
+        acc = torch.full((n, 512), float("nan"), device=x.device)
+        out = plan.forward(x[:n], ids[:n], wts[:n], acc=acc, workspace=workspace)
+        torch.cuda.synchronize()
+        return out, acc
+
+    for n in (300, 200, 300):     # 200 tokens: still the prefill kernels (>= 16 routes per expert)
+        want_o, want_a = run(n, None)
+        got_o, got_a = run(n, ws)
+        np.testing.assert_array_equal(G.bf16_bits(got_o), G.bf16_bits(want_o))
+        np.testing.assert_array_equal(got_a.cpu().numpy(), want_a.cpu().numpy())
+    check_layer(case, got_o, got_a, ew=case.experts())
+
+
 def test_zero_weight_route_equals_invalid_route(mid):
     case, plan, _ = mid
     say("invariants: zero weight vs invalid id")
