@@ -347,6 +347,43 @@ def test_repeat_runs_identical_and_inputs_untouched(mid):
     assert torch.equal(rp, plan.repacked)
 
 
+@pytest.mark.parametrize("act", ["bf16", "mxfp8"])
+def test_small_and_large_decode_schedules_give_the_same_bits(act):
+    """16 tokens take the small-batch decode schedules, 17 the large ones:
+    a row's sums do not depend on the schedule (the K split is fixed), so the
+    first 16 rows agree bit for bit.  Also: a token with no valid route, and a
+    batch with none at all (no tile; the outputs still written, +0 over the
+    NaN fill)."""
+    case = W.make_case("fold", W.LayerShape(17, 256, 128, 8, 8, 2), 77, routing="uniform", invalid_frac=0.2,
+                       act=act)
+    ids_np = case.topk_ids.copy()
+    ids_np[3] = [-1, 9]                          # token 3: no valid route (E = 8)
+    say(f"small vs large decode schedules ({act})")
+    plan, _ = G.make_plan(case)
+    x = G.to_dev(case.hidden_bits).view(torch.bfloat16)
+    ids = G.to_dev(ids_np)
+    wts = G.to_dev(case.topk_weights)
+
+    def run(n, ids_dev):
+        acc = torch.full((n, 256), float("nan"), device=x.device)
+        out = torch.full((n, 256), float("nan"), dtype=torch.bfloat16, device=x.device)
+        plan.forward(x, ids_dev, wts, out=out, acc=acc, num_tokens=n)
+        torch.cuda.synchronize()
+        return out, acc
+
+    out17, acc17 = run(17, ids)
+    out16, acc16 = run(16, ids)
+    np.testing.assert_array_equal(G.bf16_bits(out16), G.bf16_bits(out17)[:16])
+    np.testing.assert_array_equal(acc16.cpu().numpy(), acc17.cpu().numpy()[:16])
+    import dataclasses
+    c16 = dataclasses.replace(case, topk_ids=ids_np)
+    check_layer(c16, out17, acc17, tokens=range(16), ew=case.experts())
+    assert not G.bf16_bits(out16)[3].any() and not acc16[3].cpu().numpy().view(np.uint32).any()
+    none = G.to_dev(np.full_like(ids_np, -1))
+    out, acc = run(5, none)
+    assert not G.bf16_bits(out).any() and not acc.cpu().numpy().view(np.uint32).any()
+
+
 def test_prefill_workspace_with_stale_bytes_gives_the_same_bits():
     """The bf16 prefill kernels take their work items from counters in the
     workspace, which the route stage zeroes in the stream every forward: a
