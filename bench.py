@@ -333,7 +333,7 @@ def prefill_line(args):
                    "top_k": s.top_k},
         "roofline": {"bound": "mfma", "achieved": round(fc1_tflops, 1), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(fc1_tflops / peak, 4), "traffic": counter_traffic(args.workload, tag),
-                     "kernel": ("fc_pre_mx<true> (FC1, MXFP8)" if mx else "fc_pre<true,128,4> (FC1, bf16)"),
+                     "kernel": ("fc_pre_mx<true,8> (FC1, MXFP8, eight waves)" if mx else "fc_pre<true,128,4> (FC1, bf16)"),
                      "kernel_us": round(fc1_us, 2),
                      "alg_flops_per_launch": 2.0 * valid * s.hidden * 2 * s.inter},
         "layer": summ,
