@@ -104,7 +104,10 @@ moe_status moe_mxfp4_plan(const moe_mxfp4_config* cfg, const uint8_t* w13_codes,
  *                 with the fp32 token accumulator (tokens without a valid
  *                 route get +0.0)
  *   out_bf16      [T, H] bf16: overwritten with RNE_bf16(acc)
- *   workspace     caller buffer of workspace_bytes (query_sizes)
+ *   workspace     caller buffer of workspace_bytes (query_sizes); its contents
+ *                 on entry do not matter (the call sets every word it reads,
+ *                 including the work counters of the large-batch kernels,
+ *                 which its first kernel zeroes on the stream)
  * Enqueue-only: no host synchronisation and no allocation, so the call can be
  * captured in a HIP graph.  Inputs and the repacked weights are never written.
  * Concurrent calls sharing one workspace race. */
