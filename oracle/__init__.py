@@ -15,9 +15,10 @@ module):
   compare  the acceptance rule (3 bf16 ULP or 4e-3 row relative L2)
 
 Every function is pinned by ``tests/test_oracle_*.py`` against closed forms,
-library codecs, brute force and exact invariants; the one unpinned reading is
-the nibble order inside a byte (element 2j in the low nibble), which the
-pages settle without printing the verdict.
+library codecs, brute force, exact invariants and, for the MXFP4
+dequantisation including the nibble order inside a byte (element 2j in the low
+nibble, which the pages settle without printing the verdict), an independently
+written decoder (transformers' MXFP4 integration).
 """
 from .formats import (E2M1_MAGNITUDES, E4M3_MAX, bf16_bits_to_f64, dequant_mxfp4, e2m1_value,
                       e4m3_encode, e4m3_value, e8m0_value, f32_to_bf16_rne, pack_nibbles,

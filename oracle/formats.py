@@ -8,7 +8,9 @@ TEST INFRASTRUCTURE ONLY: nothing in the product path may import this module.
   byte along K ("E2M1 nibbles + E8M0 scales", batchgen PR #307, section
   "What").  Nibble order: element 2j in bits 3:0, element 2j+1 in bits 7:4.
   The pages say the order was settled against an external library but do not
-  print the verdict, so this order is a reading (parity unpinned externally).
+  print the verdict; the tests pin this order (and the whole dequantisation)
+  bit for bit against an independently written MXFP4 decoder (transformers'
+  MXFP4 integration), with the swapped order as a negative control.
 * E8M0 (shared scale): an unsigned biased exponent, value 2^(b-127); the pages
   raise on the edge bytes 0x00 and 0xFF (batchgen PR #307, repack commit:
   "exact E8M0->bf16 expansion ... edge bytes raise"), so weight scales with
