@@ -75,6 +75,8 @@ def build_plan(cid, max_tokens):
 class Batches:
     """`sets` device-resident input sets of one configuration at T tokens."""
 
+    fused = False   # also time the one-launch forward (--fused)
+
     def __init__(self, plan, cid, tokens, sets):
         import torch
         import workloads as W
@@ -142,7 +144,7 @@ class Batches:
                 "stage_ms": stage.mean(axis=0), "fc1_ms": stage[:, 1],
                 "layer_bytes": alg[:, 0].mean(), "fc1_bytes": alg[:, 1].mean(), "flops": alg[:, 2].mean(),
                 "graph_ms_per_step": self.run_graph(steps, warmup),
-                "fused_ms_per_step": self.run_fused(steps, warmup)}
+                "fused_ms_per_step": self.run_fused(steps, warmup) if self.fused else None}
 
     def run_fused(self, steps, warmup):
         """The same steps through the one-launch forward (bf16, at most 256
@@ -352,6 +354,8 @@ def main():
     p.add_argument("--no-extra", action="store_true")
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--workload", default="decode", choices=["decode"] + list(PREFILL))
+    p.add_argument("--fused", action="store_true",
+                   help="also time the one-launch (cooperative) fused forward on decode batches")
     p.add_argument("--copy-probe", action="store_true",
                    help="first copy 512 MiB with torch three times: a kernel of known bytes for counter scaling")
     args = p.parse_args()
@@ -374,6 +378,7 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    Batches.fused = args.fused
     if args.workload != "decode":
         print(json.dumps(prefill_line(args)), flush=True)
         return

@@ -159,6 +159,27 @@ moe_status moe_mxfp4_route(moe_mxfp4_plan_t plan, const int32_t* topk_ids, int32
                            int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* rowpos,
                            void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Regions of the forward workspace that hold an intermediate of the last
+ * forward on it, for checking (moe_mxfp4_workspace_region). */
+typedef enum {
+  MOE_WS_H_CODES = 0,   /* MOE_ACT_MXFP8: the requantised gated activation h as
+                           E4M3FN codes, u8 [T_max * k, I]; row r belongs to the
+                           r-th valid route in (expert, t*k+s) order (the perm
+                           of moe_mxfp4_route), rows past the valid routes are
+                           unspecified */
+  MOE_WS_H_SCALES = 1   /* MOE_ACT_MXFP8: its E8M0 bytes, u8 [T_max * k, I/32] */
+} moe_ws_region;
+
+/* Byte offset and size of a workspace region of the plan's layout, so a
+ * checker can read an intermediate back (pegainfer PR #867, commit 53edfa98:
+ * the chain's requantised activation scales are compared bit for bit).  The
+ * MXFP8 path quantises h from fp32; where the exact h sits within fp32
+ * rounding of a rounding or scale decision, either side is correct, so the
+ * layer output alone cannot show which one the kernels took.  Host only.
+ * MOE_ERR_ARG for an unknown region or a MOE_ACT_BF16 plan (which keeps h in
+ * bf16 and has neither region). */
+moe_status moe_mxfp4_workspace_region(moe_mxfp4_plan_t plan, int32_t region, size_t* offset, size_t* bytes);
+
 /* MXFP8 quantisation of a bf16 matrix [rows, cols] (cols a multiple of 32),
  * as applied to the activations in MOE_ACT_MXFP8 mode (pegainfer PR #867,
  * commit 33d22f80: gran-32 e4m3 activation quant with UE8M0 scales):

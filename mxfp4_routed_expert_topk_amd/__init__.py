@@ -11,6 +11,7 @@ Names follow the C ABI in include/moe_mxfp4.h:
   Plan(cfg, w13_codes, w13_scales, w2_codes, w2_scales)     (moe_mxfp4_plan)
   Plan.forward(hidden, topk_ids, topk_weights, out=None, acc=None)
   Plan.route(topk_ids)                  -> (counts, offsets, perm, rowpos)
+  Plan.workspace_region(region)         -> the workspace bytes of an intermediate (MXFP8 h)
   mxfp8_quantize(x_bf16)                -> (codes, scales)
   router_topk(logits, k)                -> (topk_ids, topk_weights)  (moe_router_topk)
 """
@@ -29,9 +30,12 @@ MOE_ACT_MXFP8 = 1
 STATUS_NAMES = {0: "MOE_OK", 1: "MOE_ERR_ARG", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_ALIGN", 4: "MOE_ERR_CAPACITY",
                 5: "MOE_ERR_SCALE_BYTE", 6: "MOE_ERR_WORKSPACE", 7: "MOE_ERR_UNSUPPORTED", 8: "MOE_ERR_HIP",
                 9: "MOE_ERR_TIMEOUT"}
+MOE_WS_H_CODES = 0
+MOE_WS_H_SCALES = 1
 EXPORTS = ("moe_mxfp4_query_sizes", "moe_mxfp4_plan", "moe_mxfp4_forward", "moe_mxfp4_forward_fused",
-           "moe_mxfp4_fused_status", "moe_mxfp4_route", "moe_mxfp8_quantize", "moe_router_topk",
-           "moe_mxfp4_set_stage_events", "moe_mxfp4_destroy", "moe_mxfp4_last_error")
+           "moe_mxfp4_fused_status", "moe_mxfp4_route", "moe_mxfp4_workspace_region", "moe_mxfp8_quantize",
+           "moe_router_topk", "moe_mxfp4_set_stage_events", "moe_mxfp4_destroy", "moe_mxfp4_last_error")
+_STATUS_FNS = tuple(n for n in EXPORTS if n not in ("moe_mxfp4_destroy", "moe_mxfp4_last_error"))
 
 
 class MoeError(RuntimeError):
@@ -79,6 +83,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_mxfp4_forward_fused.argtypes = [vp, vp, vp, vp, i32, vp, vp, vp, sz, vp]
     lib.moe_mxfp4_fused_status.argtypes = [vp, vp, sz, vp]
     lib.moe_mxfp4_route.argtypes = [vp, vp, i32, vp, vp, vp, vp, vp, sz, vp]
+    lib.moe_mxfp4_workspace_region.argtypes = [vp, i32, ctypes.POINTER(sz), ctypes.POINTER(sz)]
     lib.moe_mxfp8_quantize.argtypes = [vp, i32, i32, vp, vp, vp]
     lib.moe_router_topk.argtypes = [vp, i32, i32, i32, vp, vp, vp]
     lib.moe_mxfp4_set_stage_events.argtypes = [vp, ctypes.POINTER(vp), i32]
@@ -86,9 +91,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_mxfp4_destroy.restype = None
     lib.moe_mxfp4_last_error.argtypes = []
     lib.moe_mxfp4_last_error.restype = ctypes.c_char_p
-    for name in ("moe_mxfp4_query_sizes", "moe_mxfp4_plan", "moe_mxfp4_forward", "moe_mxfp4_forward_fused",
-                 "moe_mxfp4_fused_status", "moe_mxfp4_route", "moe_mxfp8_quantize", "moe_router_topk",
-                 "moe_mxfp4_set_stage_events"):
+    for name in _STATUS_FNS:
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -101,6 +104,36 @@ def _check(status: int) -> None:
 
 def _ptr(t) -> Optional[int]:
     return None if t is None else t.data_ptr()
+
+
+MOE_ERR_ARG = 1
+
+
+def _arg_error(msg: str):
+    return MoeError(MOE_ERR_ARG, msg)
+
+
+def _need(t, name: str, dtype, rows_min: int, cols: Optional[int], device, ndim: int = 2):
+    """Raise MoeError(MOE_ERR_ARG) unless `t` is a contiguous tensor of `dtype`
+    on `device`, shaped [>= rows_min, cols] (cols None: any)."""
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise _arg_error(f"{name} must be a torch.Tensor, got {type(t).__name__}")
+    if t.dtype != dtype:
+        raise _arg_error(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != ndim:
+        raise _arg_error(f"{name} must have {ndim} dimensions, got shape {tuple(t.shape)}")
+    if device is not None and t.device != device:
+        raise _arg_error(f"{name} must be on {device}, got {t.device}")
+    if not t.is_contiguous():
+        raise _arg_error(f"{name} must be contiguous")
+    if ndim == 2:
+        if t.shape[0] < rows_min:
+            raise _arg_error(f"{name} must have at least {rows_min} rows, got shape {tuple(t.shape)}")
+        if cols is not None and t.shape[1] != cols:
+            raise _arg_error(f"{name} must have {cols} columns, got shape {tuple(t.shape)}")
+    elif t.numel() < rows_min:
+        raise _arg_error(f"{name} must hold at least {rows_min} elements, got {t.numel()}")
 
 
 def _stream(stream=None) -> int:
@@ -147,13 +180,32 @@ class Plan:
         except Exception:
             pass
 
+    def _forward_args(self, hidden, topk_ids, topk_weights, out, acc, num_tokens, workspace):
+        """Check the tensors of a forward against the plan (dtype, shape, device,
+        contiguity; MoeError(MOE_ERR_ARG) otherwise) and allocate `out` if None."""
+        import torch
+        c = self.cfg
+        dev = self.workspace.device
+        if not isinstance(hidden, torch.Tensor) or hidden.dim() != 2:
+            raise _arg_error("hidden must be a 2-D torch.Tensor [T, hidden]")
+        T = hidden.shape[0] if num_tokens is None else int(num_tokens)
+        if T < 0 or T > hidden.shape[0]:
+            raise _arg_error(f"num_tokens must be in [0, {hidden.shape[0]}] (rows of hidden), got {T}")
+        _need(hidden, "hidden", torch.bfloat16, T, c.hidden, dev)
+        _need(topk_ids, "topk_ids", torch.int32, T, c.top_k, dev)
+        _need(topk_weights, "topk_weights", torch.float32, T, c.top_k, dev)
+        if out is None:
+            out = torch.empty((hidden.shape[0], c.hidden), dtype=torch.bfloat16, device=dev)
+        _need(out, "out", torch.bfloat16, T, c.hidden, dev)
+        if acc is not None:
+            _need(acc, "acc", torch.float32, T, c.hidden, dev)
+        ws = self.workspace if workspace is None else workspace
+        _need(ws, "workspace", torch.uint8, 0, None, dev, ndim=1)
+        return T, out, ws
+
     def forward(self, hidden, topk_ids, topk_weights, out=None, acc=None, num_tokens=None, stream=None,
                 workspace=None):
-        import torch
-        T = hidden.shape[0] if num_tokens is None else int(num_tokens)
-        if out is None:
-            out = torch.empty((hidden.shape[0], self.cfg.hidden), dtype=torch.bfloat16, device=hidden.device)
-        ws = self.workspace if workspace is None else workspace
+        T, out, ws = self._forward_args(hidden, topk_ids, topk_weights, out, acc, num_tokens, workspace)
         _check(load_library().moe_mxfp4_forward(self._h, _ptr(hidden), _ptr(topk_ids), _ptr(topk_weights), T,
                                                 _ptr(acc), _ptr(out), _ptr(ws), ws.numel(), _stream(stream)))
         return out
@@ -161,11 +213,7 @@ class Plan:
     def forward_fused(self, hidden, topk_ids, topk_weights, out=None, acc=None, num_tokens=None, stream=None,
                       workspace=None):
         """The same forward in one kernel launch (bf16 plans, at most 256 routes)."""
-        import torch
-        T = hidden.shape[0] if num_tokens is None else int(num_tokens)
-        if out is None:
-            out = torch.empty((hidden.shape[0], self.cfg.hidden), dtype=torch.bfloat16, device=hidden.device)
-        ws = self.workspace if workspace is None else workspace
+        T, out, ws = self._forward_args(hidden, topk_ids, topk_weights, out, acc, num_tokens, workspace)
         _check(load_library().moe_mxfp4_forward_fused(self._h, _ptr(hidden), _ptr(topk_ids), _ptr(topk_weights),
                                                       T, _ptr(acc), _ptr(out), _ptr(ws), ws.numel(),
                                                       _stream(stream)))
@@ -178,8 +226,13 @@ class Plan:
 
     def route(self, topk_ids, num_tokens=None, stream=None):
         import torch
+        dev = self.workspace.device
+        if not isinstance(topk_ids, torch.Tensor) or topk_ids.dim() != 2:
+            raise _arg_error("topk_ids must be a 2-D torch.Tensor [T, top_k]")
         T = topk_ids.shape[0] if num_tokens is None else int(num_tokens)
-        dev = topk_ids.device
+        if T < 0 or T > topk_ids.shape[0]:
+            raise _arg_error(f"num_tokens must be in [0, {topk_ids.shape[0]}] (rows of topk_ids), got {T}")
+        _need(topk_ids, "topk_ids", torch.int32, T, self.cfg.top_k, dev)
         E, n = self.cfg.num_experts, max(1, T * self.cfg.top_k)
         counts = torch.empty(E, dtype=torch.int32, device=dev)
         offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
@@ -189,6 +242,15 @@ class Plan:
                                               _ptr(rowpos), _ptr(self.workspace), self.workspace.numel(),
                                               _stream(stream)))
         return counts, offsets, perm, rowpos
+
+    def workspace_region(self, region, workspace=None):
+        """The uint8 view of `workspace` (default: the plan's) holding an
+        intermediate of the last forward on it (MOE_WS_H_CODES: MXFP8 h codes
+        [T_max*k, I]; MOE_WS_H_SCALES: their E8M0 bytes [T_max*k, I/32])."""
+        off, nb = ctypes.c_size_t(), ctypes.c_size_t()
+        _check(load_library().moe_mxfp4_workspace_region(self._h, int(region), ctypes.byref(off), ctypes.byref(nb)))
+        ws = self.workspace if workspace is None else workspace
+        return ws[off.value: off.value + nb.value]
 
     def set_stage_events(self, events):
         """events: list of 5 torch.cuda.Event(enable_timing=True) or None to stop."""
@@ -209,17 +271,25 @@ def router_topk(logits, top_k, ids=None, weights=None, stream=None):
     """topk_ids int32 [T, k] and topk_weights fp32 [T, k] from fp32 logits [T, E]
     (moe_router_topk)."""
     import torch
+    if not isinstance(logits, torch.Tensor) or logits.dim() != 2:
+        raise _arg_error("logits must be a 2-D torch.Tensor [T, num_experts]")
     T, E = logits.shape
+    _need(logits, "logits", torch.float32, T, E, logits.device)
     ids = torch.empty((T, top_k), dtype=torch.int32, device=logits.device) if ids is None else ids
     weights = torch.empty((T, top_k), dtype=torch.float32, device=logits.device) if weights is None else weights
+    _need(ids, "topk_ids", torch.int32, T, top_k, logits.device)
+    _need(weights, "topk_weights", torch.float32, T, top_k, logits.device)
     _check(load_library().moe_router_topk(_ptr(logits), T, E, top_k, _ptr(ids), _ptr(weights), _stream(stream)))
     return ids, weights
 
 
 def mxfp8_quantize(x_bf16, stream=None):
     import torch
+    if not isinstance(x_bf16, torch.Tensor) or x_bf16.dim() != 2:
+        raise _arg_error("x must be a 2-D torch.Tensor [rows, cols]")
     rows, cols = x_bf16.shape
+    _need(x_bf16, "x", torch.bfloat16, rows, cols, x_bf16.device)
     codes = torch.empty((rows, cols), dtype=torch.uint8, device=x_bf16.device)
-    scales = torch.empty((rows, cols // 32), dtype=torch.uint8, device=x_bf16.device)
+    scales = torch.empty((rows, max(cols // 32, 0)), dtype=torch.uint8, device=x_bf16.device)
     _check(load_library().moe_mxfp8_quantize(_ptr(x_bf16), rows, cols, _ptr(codes), _ptr(scales), _stream(stream)))
     return codes, scales

@@ -427,6 +427,21 @@ moe_status moe_mxfp4_route(moe_mxfp4_plan_t p, const int32_t* topk_ids, int32_t 
   return ok();
 }
 
+moe_status moe_mxfp4_workspace_region(moe_mxfp4_plan_t p, int32_t region, size_t* offset, size_t* bytes) {
+  if (!p) return fail(MOE_ERR_ARG, "plan is null");
+  if (!offset || !bytes) return fail(MOE_ERR_ARG, "offset and bytes must not be null");
+  if (p->cfg.act != MOE_ACT_MXFP8)
+    return fail(MOE_ERR_ARG, "workspace regions of h exist for MOE_ACT_MXFP8 plans only, got act=%d", p->cfg.act);
+  const moe::Layout& L = p->L;
+  const size_t R = (size_t)L.Rmax;
+  switch (region) {
+    case MOE_WS_H_CODES: *offset = L.ws_hq; *bytes = R * L.I; break;
+    case MOE_WS_H_SCALES: *offset = L.ws_hs; *bytes = R * (L.I / 32); break;
+    default: return fail(MOE_ERR_ARG, "region must be MOE_WS_H_CODES (0) or MOE_WS_H_SCALES (1), got %d", region);
+  }
+  return ok();
+}
+
 moe_status moe_mxfp8_quantize(const uint16_t* x, int32_t rows, int32_t cols, uint8_t* codes, uint8_t* scales,
                               hipStream_t stream) {
   if (rows < 0) return fail(MOE_ERR_ARG, "rows must be >= 0, got %d", rows);

@@ -21,7 +21,9 @@ MXFP8 variant: x (before FC1) and h (before FC2) are replaced by their MXFP8
 round trip, blocks of 32 along K (``mxfp8_quantize``).  x is exact, so its
 codes are unique; h is not: an implementation that holds h in fp32 may land
 on the other side of a rounding decision where the exact h sits within fp32
-rounding of one, and ``forward(..., with_spread=True)`` bounds the effect.
+rounding of one.  ``mxfp8_requant_check`` decides whether a given
+quantisation of h is one of the correct ones, and ``forward(...,
+h_requant=...)`` evaluates the rest of the layer from it.
 
 The whole-layer results are reached exactly by the definition; the per-expert
 grouping below is only a way to evaluate it: each route's y is computed from
@@ -106,16 +108,26 @@ def _roundtrip_at(blocks: np.ndarray, exps: np.ndarray) -> np.ndarray:
     return np.ldexp(e4m3_value(e4m3_encode(np.ldexp(blocks, -exps[:, :, None]))), exps[:, :, None])
 
 
-def mxfp8_roundtrip_spread(v: np.ndarray, dv: np.ndarray):
-    """(round trip of v, spread): spread[i] bounds |rt(v')[i] - rt(v)[i]| over
-    every v' with |v' - v| <= dv elementwise.
+def mxfp8_requant_check(v: np.ndarray, dv: np.ndarray, codes: np.ndarray, scales: np.ndarray) -> dict:
+    """Whether (codes, scales) is an MXFP8 quantisation of some v' with
+    |v' - v| <= dv elementwise, element by element.
 
-    The quantiser is a step function: a value within dv of a rounding midpoint,
-    or a block whose maximum is within its elements' dv of a scale boundary
-    448 * 2^e, has more than one correct round trip when v itself is only known
-    to within dv.  Each block exponent the block maximum can take inside its
-    interval is tried; at each, the code of v' lies between the codes of v - dv
-    and v + dv (rounding to nearest even and saturation are monotone).
+    The quantiser is a step function of its input, so a value known only to
+    within dv has more than one correct quantisation where the interval
+    [v - dv, v + dv] straddles a decision: an E4M3 rounding midpoint of an
+    element, or a scale boundary 448 * 2^e of its block maximum.  The block
+    exponents any v' can give lie in [e_lo, e_hi] (those of the smallest and
+    largest block maximum in the interval; the exponent rule is monotone), and
+    at a given exponent the element's code lies between the codes of v - dv
+    and v + dv (saturation and round-to-nearest-even are monotone).  An
+    element is admissible when its block's scale byte is a reachable exponent
+    and its value lies between those two codes' values at that exponent.
+
+    Returns a dict: ``values`` (the dequantised (codes, scales)), ``rt`` (the
+    round trip of v itself), ``admissible`` and ``ambiguous`` (bool arrays:
+    more than one correct value exists for the element), and the counts
+    ``n``, ``n_ambiguous``, ``n_differ`` (admissible values other than rt) and
+    ``n_bad`` (inadmissible elements).
     """
     x = np.asarray(v, dtype=np.float64)
     d = np.broadcast_to(np.abs(np.asarray(dv, dtype=np.float64)), x.shape)
@@ -125,33 +137,58 @@ def mxfp8_roundtrip_spread(v: np.ndarray, dv: np.ndarray):
     nb = k // MXFP8_BLOCK
     blocks = x.reshape(-1, nb, MXFP8_BLOCK)
     dblk = d.reshape(-1, nb, MXFP8_BLOCK)
-    mag = np.abs(blocks)
+    n = blocks.shape[0]
     expo = np.vectorize(mxfp8_scale_exponent, otypes=[np.int64])
     if blocks.size == 0:
-        return x.copy(), np.zeros_like(x)
+        z = np.zeros(x.shape, bool)
+        return dict(values=x.copy(), rt=x.copy(), admissible=~z, ambiguous=z, n=0, n_ambiguous=0,
+                    n_differ=0, n_bad=0)
+    mag = np.abs(blocks)
     e0 = expo(mag.max(axis=2))
     e_lo = expo(np.maximum(mag - dblk, 0.0).max(axis=2))
     e_hi = expo((mag + dblk).max(axis=2))
     rt = _roundtrip_at(blocks, e0)
-    spread = np.zeros_like(rt)
-    for off in range(int((e_hi - e_lo).max()) + 1):
-        e = np.minimum(e_lo + off, e_hi)
-        lo = _roundtrip_at(blocks - dblk, e)
-        hi = _roundtrip_at(blocks + dblk, e)
-        spread = np.maximum(spread, np.maximum(np.abs(lo - rt), np.abs(hi - rt)))
-    return rt.reshape(x.shape), spread.reshape(x.shape)
+    dev_e = np.asarray(scales, dtype=np.int64).reshape(n, nb) - 127
+    got = mxfp8_dequantize(np.asarray(codes, dtype=np.uint8).reshape(n, nb * MXFP8_BLOCK),
+                           np.asarray(scales, dtype=np.uint8).reshape(n, nb)).reshape(n, nb, MXFP8_BLOCK)
+    lo = _roundtrip_at(blocks - dblk, dev_e)
+    hi = _roundtrip_at(blocks + dblk, dev_e)
+    reachable = ((dev_e >= e_lo) & (dev_e <= e_hi))[:, :, None]
+    with np.errstate(invalid="ignore"):
+        admissible = reachable & (got >= lo) & (got <= hi)
+    # more than one correct value: several reachable exponents, or two codes at the exponent of v
+    amb = (e_lo != e_hi)[:, :, None] | (_roundtrip_at(blocks - dblk, e0) != _roundtrip_at(blocks + dblk, e0))
+    differ = admissible & (got != rt)
+    shape = x.shape
+    return dict(values=got.reshape(shape), rt=rt.reshape(shape), admissible=admissible.reshape(shape),
+                ambiguous=amb.reshape(shape), n=int(x.size), n_ambiguous=int(amb.sum()),
+                n_differ=int(differ.sum()), n_bad=int((~admissible).sum()))
 
 
 # fp32 rounding of the h that the MXFP8 path requantises.  A K-long dot product
-# evaluated as MFMA steps of 128 products (an adder tree of depth 7 with fp32
-# rounding) chained through an fp32 accumulator differs from the exact sum by
-# at most (7 + K/128) * 2^-24 * sum|terms|; silu and the gate product add a
-# few more roundings.  Twice that is the allowance used for h.
+# evaluated as MFMA steps of at most 128 exact products (an adder tree of depth
+# at most 7 with fp32 rounding) chained through an fp32 accumulator, with a few
+# more fp32 additions for K split over waves, differs from the exact sum by at
+# most (7 + ceil(K/128) + 4) * 2^-24 * sum|terms|; twice that is the allowance
+# (it also covers truncating instead of rounding additions).  silu and the gate
+# product add a few roundings of h on top (see ``h_uncertainty``).
 FP32_EPS = 2.0 ** -24
 
 
 def fp32_dot_bound(k: int) -> float:
     return 2.0 * (7 + -(-k // 128) + 4) * FP32_EPS
+
+
+def h_uncertainty(x_rows: np.ndarray, w13: np.ndarray, g: np.ndarray, u: np.ndarray, h: np.ndarray) -> np.ndarray:
+    """Bound on |h_fp32 - h| for an fp32 evaluation of h = silu(g) * u whose
+    g and u are fp32 dot products (``fp32_dot_bound``): |silu'| <= 1.1, so
+    |dh| <= 1.1 dg (|u| + du) + |silu(g)| du, plus a few fp32 roundings of
+    silu and the product."""
+    inter = g.shape[1]
+    gam = fp32_dot_bound(x_rows.shape[1])
+    absum = np.abs(x_rows) @ np.abs(w13).T            # sum of |terms| of every dot product
+    dg, du = gam * absum[:, :inter], gam * absum[:, inter:]
+    return 1.1 * dg * (np.abs(u) + du) + np.abs(silu(g)) * du + 8 * FP32_EPS * np.abs(h)
 
 
 # --------------------------------------------------------------------------- forward
@@ -162,13 +199,14 @@ def _expert_getter(weights: ExpertSource):
     return lambda e: (w13c[e], w13s[e], w2c[e], w2s[e])
 
 
-def expert_mlp(x_rows: np.ndarray, w13c, w13s, w2c, w2s, act: str = "bf16", with_spread: bool = False):
+def expert_mlp(x_rows: np.ndarray, w13c, w13s, w2c, w2s, act: str = "bf16", h_requant=None):
     """y rows for one expert: W2 (silu(w1 x) * (w3 x)), fp64 throughout.
 
-    ``with_spread`` (MXFP8 only) also returns a per-element bound on how far y
-    can move when h carries fp32 rounding (``fp32_dot_bound``) and so may be
-    requantised on the other side of a rounding decision: |W2| times the
-    round-trip spread of h.  For bf16 the bound is zero.
+    MXFP8: h goes through its MXFP8 round trip before W2.  ``h_requant``
+    (optional) replaces that round trip: it is called as ``h_requant(h, dh)``
+    with the exact h rows and ``h_uncertainty`` of an fp32 evaluation, and
+    returns the round-trip values to use (a checker passes the quantisation an
+    implementation made, after ``mxfp8_requant_check`` has found it correct).
     """
     w13 = dequant_mxfp4(w13c, w13s)                  # [2I, H]
     inter = w13.shape[0] // 2
@@ -176,36 +214,27 @@ def expert_mlp(x_rows: np.ndarray, w13c, w13s, w2c, w2s, act: str = "bf16", with
     g, u = gu[:, :inter], gu[:, inter:]
     h = silu(g) * u
     w2 = dequant_mxfp4(w2c, w2s)                      # [H, I]
-    spread = None
     if act == "mxfp8":
-        if with_spread:
-            gam = fp32_dot_bound(x_rows.shape[1])
-            absum = np.abs(x_rows) @ np.abs(w13).T    # sum of |terms| of every dot product
-            dg, du = gam * absum[:, :inter], gam * absum[:, inter:]
-            # |silu'| <= 1.1: |dh| <= 1.1 dg (|u| + du) + |silu(g)| du, plus rounding of h
-            dh = 1.1 * dg * (np.abs(u) + du) + np.abs(silu(g)) * du + 8 * FP32_EPS * np.abs(h)
-            h, sp = mxfp8_roundtrip_spread(h, dh)
-            spread = sp @ np.abs(w2).T
-        else:
+        if h_requant is None:
             h = mxfp8_roundtrip(h)
-    y = h @ w2.T                                      # [r, H]
-    if with_spread:
-        return y, (spread if spread is not None else np.zeros_like(y))
-    return y
+        else:
+            h = h_requant(h, h_uncertainty(x_rows, w13, g, u, h))
+    return h @ w2.T                                   # [r, H]
 
 
 def forward(hidden_bits: np.ndarray, topk_ids: np.ndarray, topk_weights: np.ndarray,
             weights: ExpertSource, experts: int, act: str = "bf16",
-            tokens: Optional[Sequence[int]] = None, with_spread: bool = False):
+            tokens: Optional[Sequence[int]] = None, h_requant=None, pool=None):
     """fp64 accumulator [len(tokens) or T, H] of the MoE layer.
 
     ``weights``: stacked checkpoint-layout arrays (w13_codes [E,2I,H/2],
     w13_scales [E,2I,H/32], w2_codes [E,H,I/2], w2_scales [E,H,I/32]) or a
     callable returning one expert's four arrays.  ``tokens``: evaluate only
-    these tokens (rows of the result follow this order).  ``with_spread``:
-    also return sum_s |w[t,s]| * (the y bound of ``expert_mlp``), the most
-    an fp32 evaluation may differ from the accumulator through rounding
-    decisions of the MXFP8 requantisation of h (zero for bf16).
+    these tokens (rows of the result follow this order).  ``h_requant``
+    (MXFP8 only): called as ``h_requant(e, routes, h, dh)`` per expert, with
+    routes the (token, slot) pairs of h's rows; see ``expert_mlp``.  ``pool``:
+    an executor whose ``map`` evaluates the experts' rows concurrently (each
+    expert's rows are independent; the slot-order sum below is unchanged).
     """
     if act not in ("bf16", "mxfp8"):
         raise ValueError(f"unknown activation format {act!r}")
@@ -226,22 +255,25 @@ def forward(hidden_bits: np.ndarray, topk_ids: np.ndarray, topk_weights: np.ndar
             e = int(ids[t, s])
             if 0 <= e < experts:
                 by_expert.setdefault(e, []).append((i, s))
-    y, yb = {}, {}
-    for e in sorted(by_expert):
+    order = sorted(by_expert)
+
+    def one(e):
         rows = by_expert[e]
-        res = expert_mlp(x[[i for i, _ in rows]], *get(e), act=act, with_spread=with_spread)
-        ye, be = res if with_spread else (res, None)
-        for j, key in enumerate(rows):
+        hr = None
+        if h_requant is not None:
+            routes = [(sel[i], s) for i, s in rows]
+            hr = lambda h, dh: h_requant(e, routes, h, dh)
+        return expert_mlp(x[[i for i, _ in rows]], *get(e), act=act, h_requant=hr)
+
+    results = list(pool.map(one, order)) if pool is not None else [one(e) for e in order]
+    y = {}
+    for e, ye in zip(order, results):
+        for j, key in enumerate(by_expert[e]):
             y[key] = ye[j]
-            if with_spread:
-                yb[key] = be[j]
 
     acc = np.zeros((len(sel), hidden), dtype=np.float64)
-    bound = np.zeros_like(acc)
     for i, t in enumerate(sel):
         for s in range(k):                            # ascending slot order
             if (i, s) in y:
                 acc[i] += wts[t, s] * y[(i, s)]
-                if with_spread:
-                    bound[i] += abs(wts[t, s]) * yb[(i, s)]
-    return (acc, bound) if with_spread else acc
+    return acc

@@ -2,10 +2,18 @@
 
 Routing and repack: bit-exact.  Layer outputs: every row within 3 bf16 ULP
 or 4e-3 relative L2 of the oracle (oracle.check_rows), and out_bf16 equal
-bit for bit to RNE_bf16(acc_fp32).  Small shapes are compared in full; the
-full-size configurations on sampled tokens the oracle evaluates one by one.
+bit for bit to RNE_bf16(acc_fp32).  Every token of every case is compared,
+the full-size configurations included (the oracle evaluates the experts on a
+thread pool).  MXFP8 path: the device's requantised h (E4M3 codes and E8M0
+bytes, read back from the workspace) must equal the oracle's MXFP8 of the
+exact h except where the oracle proves the decision ambiguous (the exact h
+within fp32 evaluation error of a rounding or scale decision); the layer is
+then checked by the plain rule against the oracle evaluated from that h.
 """
+import os
 import sys
+import threading
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 import pytest
@@ -31,24 +39,89 @@ def need_gpu():
     moe.load_library()
 
 
-def check_layer(case, out, acc, tokens=None, ew=None):
-    """Compare the device outputs of `tokens` with the oracle."""
+class _OraclePool:
+    """Threads for the oracle's per-expert evaluations (numpy releases the GIL
+    in the dequantisation and the products; BLAS stays single-threaded
+    inside), printing a progress line every 64 experts."""
+
+    def __init__(self):
+        self.ex = ThreadPoolExecutor(max(1, min(16, os.cpu_count() or 1)))
+
+    def map(self, fn, items):
+        items = list(items)
+        out = []
+        for i, r in enumerate(self.ex.map(fn, items)):
+            out.append(r)
+            if (i + 1) % 64 == 0:
+                say(f"  oracle: {i + 1}/{len(items)} experts")
+        return out
+
+
+_pool = []
+
+
+def oracle_pool():
+    if not _pool:
+        _pool.append(_OraclePool())
+    return _pool[0]
+
+
+def reference(case, tokens=None, ew=None, h_requant=None):
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(1, "blas"):
+        return oracle.forward(case.hidden_bits, case.topk_ids, case.topk_weights,
+                              ew if ew is not None else case.expert, case.shape.experts, act=case.act,
+                              tokens=tokens, h_requant=h_requant, pool=oracle_pool())
+
+
+def device_h_requant(case, plan, stats, workspace=None):
+    """oracle.forward's h_requant hook: the device's MXFP8 h of each route (row
+    rowpos[t*k+s] of the workspace regions, rowpos from the oracle's route
+    sort), checked element by element by oracle.mxfp8_requant_check; the
+    counts go to `stats`."""
+    s = case.shape
+    rows_all = plan.cfg.max_tokens * s.top_k
+    hq = plan.workspace_region(moe.MOE_WS_H_CODES, workspace).view(rows_all, s.inter).cpu().numpy()
+    hs = plan.workspace_region(moe.MOE_WS_H_SCALES, workspace).view(rows_all, s.inter // 32).cpu().numpy()
+    rowpos = oracle.route_sort(case.topk_ids, s.experts)[3]
+    lock = threading.Lock()
+
+    def take(e, routes, h, dh):
+        rows = [int(rowpos[t * s.top_k + sl]) for t, sl in routes]
+        r = oracle.mxfp8_requant_check(h, dh, hq[rows], hs[rows])
+        with lock:
+            for key in ("n", "n_ambiguous", "n_differ", "n_bad"):
+                stats[key] += r[key]
+        return r["values"]
+    return take
+
+
+def check_layer(case, out, acc, tokens=None, ew=None, plan=None, workspace=None):
+    """Compare the device outputs of `tokens` (default: all) with the oracle.
+    MXFP8 needs the plan: its workspace holds the forward's requantised h."""
     sel = list(range(case.shape.tokens)) if tokens is None else list(tokens)
-    # MXFP8: h is requantised from fp32 on the device, so where the exact h lies
-    # within fp32 rounding of an E4M3 rounding or scale decision either side
-    # is correct; the oracle bounds that spread per element (zero for bf16).
-    ref, spread = oracle.forward(case.hidden_bits, case.topk_ids, case.topk_weights,
-                                 ew if ew is not None else case.expert, case.shape.experts, act=case.act,
-                                 tokens=sel, with_spread=True)
+    stats = None
+    hook = None
+    if case.act == "mxfp8":
+        assert plan is not None, "the MXFP8 check reads the forward's h from the plan's workspace"
+        stats = dict(n=0, n_ambiguous=0, n_differ=0, n_bad=0)
+        hook = device_h_requant(case, plan, stats, workspace)
+    ref = reference(case, sel, ew, hook)
+    if stats is not None:
+        say(f"  h codes: {stats['n']} checked, {stats['n_ambiguous']} ambiguous, "
+            f"{stats['n_differ']} taken the other correct way, {stats['n_bad']} wrong")
+        assert stats["n_bad"] == 0, f"{case.name}: {stats['n_bad']} requantised h codes are not a correct MXFP8 of h"
     out_bits = G.bf16_bits(out)[sel]
     out_v = oracle.bf16_bits_to_f64(out_bits)
-    r_out = oracle.check_rows(out_v, ref, spread=spread)
+    r_out = oracle.check_rows(out_v, ref)
     assert r_out["pass"], f"{case.name} out: {r_out}"
     if acc is not None:
         acc_np = acc.cpu().numpy()[sel]
-        r_acc = oracle.check_rows(acc_np, ref, spread=spread)
+        r_acc = oracle.check_rows(acc_np, ref)
         assert r_acc["pass"], f"{case.name} acc: {r_acc}"
         np.testing.assert_array_equal(out_bits, oracle.f32_to_bf16_rne(acc_np))
+    if stats is not None:
+        r_out["h_codes"] = stats
     return r_out
 
 
@@ -174,7 +247,7 @@ def test_forward_duplicate_expert_ids():
     case = W.Case(base.name, shape, base.seed, base.hidden_bits, ids, base.topk_weights, 120, 130)
     plan, _ = G.make_plan(case)
     out, acc = G.run_forward(plan, case)
-    check_layer(case, out, acc, ew=case.experts())
+    check_layer(case, out, acc, ew=case.experts(), plan=plan)
 
 
 @pytest.mark.parametrize("name,make", SMALL, ids=[s[0] for s in SMALL])
@@ -184,7 +257,7 @@ def test_forward_small_full(name, make):
     say(f"forward {name} T={s.tokens} H={s.hidden} I={s.inter} E={s.experts} k={s.top_k} act={case.act}")
     plan, _ = G.make_plan(case)
     out, acc = G.run_forward(plan, case, nan_acc=True)
-    r = check_layer(case, out, acc, ew=case.experts())
+    r = check_layer(case, out, acc, ew=case.experts(), plan=plan)
     say(f"  max_ulp={r['max_ulp']:.2f} max_rel_l2={r['max_rel_l2']:.2e}")
     if case.act == "bf16" and s.tokens * s.top_k <= FUSED_MAX_ROUTES:
         assert_fused_equal(plan, case, out, acc, ew=case.experts())
@@ -207,22 +280,6 @@ def big_plan(cid, case, max_tokens):
     return _plans[key]
 
 
-def sampled_tokens(case, n):
-    T = case.shape.tokens
-    ids = case.topk_ids
-    picks = [0, T - 1]
-    if n > 2:
-        # a token with an invalid route, and one routed to the hottest expert
-        bad = np.nonzero(((ids < 0) | (ids >= case.shape.experts)).any(axis=1))[0]
-        if bad.size:
-            picks.append(int(bad[len(bad) // 2]))
-        valid = ids[(ids >= 0) & (ids < case.shape.experts)]
-        if valid.size:
-            hot = np.bincount(valid).argmax()
-            picks.append(int(np.nonzero((ids == hot).any(axis=1))[0][-1]))
-    return sorted(set(picks)) if T > 1 else [0]
-
-
 @pytest.mark.parametrize("m", W.DECODE_M)
 def test_forward_decode(m):
     case = W.config_case(1, m=m)
@@ -230,9 +287,8 @@ def test_forward_decode(m):
     plan = big_plan(1, case, max(W.DECODE_M))
     out, acc = G.run_forward(plan, case)
     assert torch.isfinite(acc).all()
-    toks = sampled_tokens(case, 2)
-    r = check_layer(case, out, acc, tokens=toks)
-    say(f"  tokens {toks}: max_ulp={r['max_ulp']:.2f} max_rel_l2={r['max_rel_l2']:.2e}")
+    r = check_layer(case, out, acc)
+    say(f"  all {m} tokens: max_ulp={r['max_ulp']:.2f} max_rel_l2={r['max_rel_l2']:.2e}")
     if m * case.shape.top_k <= FUSED_MAX_ROUTES:
         assert_fused_equal(plan, case, out, acc)
 
@@ -263,13 +319,15 @@ def test_forward_decode_fused_at_its_limit():
     plan = big_plan(1, case, max(W.DECODE_M))
     out, acc = G.run_forward(plan, case)
     assert_fused_equal(plan, case, out, acc)
-    toks = sampled_tokens(case, 3)
-    r = check_layer(case, out, acc, tokens=toks)
-    say(f"  tokens {toks}: max_ulp={r['max_ulp']:.2f} max_rel_l2={r['max_rel_l2']:.2e}")
+    r = check_layer(case, out, acc)
+    say(f"  all 32 tokens: max_ulp={r['max_ulp']:.2f} max_rel_l2={r['max_rel_l2']:.2e}")
 
 
 @pytest.mark.parametrize("cid", [2, 3, 4])
 def test_forward_prefill(cid):
+    """Every token of the prefill configurations against the oracle: every XCD
+    chunk of the persistent work list, every tile of the most popular Zipf
+    expert, the tiles dealt round-robin on the MXFP8 path."""
     case = W.config_case(cid)
     say(f"forward config {cid} ({case.name}) T={case.shape.tokens} E={case.shape.experts} act={case.act}")
     plan = big_plan(cid, case, case.shape.tokens)
@@ -277,12 +335,11 @@ def test_forward_prefill(cid):
     # the accumulator started as NaN for the fused-sum stress: all of it is overwritten
     assert torch.isfinite(acc).all() and torch.isfinite(out.float()).all()
     np.testing.assert_array_equal(G.bf16_bits(out), oracle.f32_to_bf16_rne(acc.cpu().numpy()))
-    toks = sampled_tokens(case, 3)
-    r = check_layer(case, out, acc, tokens=toks)
-    say(f"  tokens {toks}: max_ulp={r['max_ulp']:.2f} max_rel_l2={r['max_rel_l2']:.2e}")
+    r = check_layer(case, out, acc, plan=plan)
+    say(f"  all {case.shape.tokens} tokens: max_ulp={r['max_ulp']:.2f} max_rel_l2={r['max_rel_l2']:.2e}")
 
 
-# ------------------------------------------------------------------ the pages' K3 expert shapes (sampled tokens)
+# ------------------------------------------------------------------ the pages' K3 expert shapes
 @pytest.mark.parametrize("m,act", [(1, "bf16"), (16, "bf16"), (128, "bf16"), (512, "bf16"), (512, "mxfp8")])
 def test_forward_k3_shapes(m, act):
     """Hidden 3584, intermediate 3072, top-16, 224 of 896 experts: decode buckets
@@ -303,9 +360,8 @@ def test_forward_k3_shapes(m, act):
     np.testing.assert_array_equal(G.bf16_bits(out), oracle.f32_to_bf16_rne(acc.cpu().numpy()))
     if act == "bf16" and m * case.shape.top_k <= FUSED_MAX_ROUTES:
         assert_fused_equal(_plans[key], case, out, acc)
-    toks = sampled_tokens(case, 3)
-    r = check_layer(case, out, acc, tokens=toks)
-    say(f"  tokens {toks}: max_ulp={r['max_ulp']:.2f} max_rel_l2={r['max_rel_l2']:.2e}")
+    r = check_layer(case, out, acc, plan=_plans[key])
+    say(f"  all {m} tokens: max_ulp={r['max_ulp']:.2f} max_rel_l2={r['max_rel_l2']:.2e}")
 
 
 # ------------------------------------------------------------------ exact invariants (bitwise on the device)
@@ -371,13 +427,12 @@ def test_small_and_large_decode_schedules_give_the_same_bits(act):
         torch.cuda.synchronize()
         return out, acc
 
+    import dataclasses
     out17, acc17 = run(17, ids)
+    check_layer(dataclasses.replace(case, topk_ids=ids_np), out17, acc17, ew=case.experts(), plan=plan)
     out16, acc16 = run(16, ids)
     np.testing.assert_array_equal(G.bf16_bits(out16), G.bf16_bits(out17)[:16])
     np.testing.assert_array_equal(acc16.cpu().numpy(), acc17.cpu().numpy()[:16])
-    import dataclasses
-    c16 = dataclasses.replace(case, topk_ids=ids_np)
-    check_layer(c16, out17, acc17, tokens=range(16), ew=case.experts())
     assert not G.bf16_bits(out16)[3].any() and not acc16[3].cpu().numpy().view(np.uint32).any()
     none = G.to_dev(np.full_like(ids_np, -1))
     out, acc = run(5, none)
@@ -499,8 +554,17 @@ def test_errors_are_reported(mid):
     ids = G.to_dev(case.topk_ids)
     wts = G.to_dev(case.topk_weights)
     with pytest.raises(moe.MoeError) as ei:
-        plan.forward(x, ids, wts, num_tokens=41)
+        plan.forward(x, ids, wts, num_tokens=41)          # more tokens than rows: the binding refuses
+    assert ei.value.status == 1 and "num_tokens must be in [0, 40]" in ei.value.message
+    x41 = torch.zeros((41, 512), dtype=torch.bfloat16, device=x.device)
+    ids41 = torch.zeros((41, 3), dtype=torch.int32, device=x.device)
+    wts41 = torch.zeros((41, 3), dtype=torch.float32, device=x.device)
+    with pytest.raises(moe.MoeError) as ei:
+        plan.forward(x41, ids41, wts41)                   # more tokens than the plan's capacity: the library
     assert ei.value.status == 4 and "exceeds" in ei.value.message
+    with pytest.raises(moe.MoeError) as ei:
+        plan.forward(x, ids.long(), wts)                  # torch.topk's int64 ids
+    assert ei.value.status == 1 and "topk_ids must be torch.int32" in ei.value.message
     with pytest.raises(moe.MoeError) as ei:
         plan.forward(x, ids, wts, workspace=plan.workspace[: plan.workspace_bytes - 256])
     assert ei.value.status == 6
@@ -513,6 +577,40 @@ def test_errors_are_reported(mid):
     plan.forward(x, ids, wts, out=out, num_tokens=0)
     torch.cuda.synchronize()
     assert (out == 7.0).all()
+
+
+# ------------------------------------------------------------------ negative control on the device
+def _swap_nibbles(t):
+    return ((t >> 4) | (t << 4)).to(torch.uint8)
+
+
+@pytest.mark.parametrize("act,T", [("bf16", 40), ("bf16", 300), ("mxfp8", 40), ("mxfp8", 300)])
+def test_negative_control_swapped_nibbles_fail_the_check(act, T):
+    """A plan over the same weights with the two E2M1 codes of every byte
+    swapped must fail the parity check by a wide margin (pegainfer PR #867,
+    commit 53edfa98: a flipped-nibble control fails at rel_l2 ~1.1): every row
+    above 0.5 relative L2 against the oracle of the true weights, and on the
+    MXFP8 path most requantised h codes inadmissible.  40 tokens take the
+    16-row kernels, 300 the 128-row-tile kernels."""
+    case = W.make_case(f"neg_{act}", W.LayerShape(T, 7168, 2048, 8, 12, 4), 91, routing="uniform", act=act)
+    say(f"negative control: swapped nibbles, act={act}, T={T}")
+    w = G.upload_experts(case)
+    plan, _ = G.make_plan(case, weights=[_swap_nibbles(w[0]), w[1], _swap_nibbles(w[2]), w[3]])
+    out, acc = G.run_forward(plan, case)
+    assert torch.isfinite(acc).all()
+    stats = dict(n=0, n_ambiguous=0, n_differ=0, n_bad=0)
+    hook = device_h_requant(case, plan, stats) if act == "mxfp8" else None
+    ref = reference(case, h_requant=hook)
+    rl2 = [oracle.rel_l2(a, b) for a, b in zip(acc.cpu().numpy(), ref) if np.linalg.norm(b) > 0]
+    say(f"  rel_l2 min {min(rl2):.2f} median {np.median(rl2):.2f}; h codes wrong: {stats['n_bad']} of {stats['n']}")
+    assert min(rl2) > 0.5
+    assert not oracle.check_rows(acc.cpu().numpy(), ref)["pass"]
+    if act == "mxfp8":
+        assert stats["n_bad"] > 0.5 * stats["n"]
+    # the same plan over the true weights passes
+    plan2, _ = G.make_plan(case, weights=w)
+    out2, acc2 = G.run_forward(plan2, case)
+    check_layer(case, out2, acc2, plan=plan2)
 
 
 # ------------------------------------------------------------------ the one-launch (fused) decode forward

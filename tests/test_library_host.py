@@ -6,6 +6,7 @@ import os
 import re
 
 import pytest
+import torch
 
 import mxfp4_routed_expert_topk_amd as moe
 
@@ -123,3 +124,79 @@ def test_router_argument_errors(lib):
 
 def test_destroy_null_is_a_noop(lib):
     lib.moe_mxfp4_destroy(None)
+
+
+def test_workspace_region_argument_errors(lib):
+    off, nb = ctypes.c_size_t(), ctypes.c_size_t()
+    assert lib.moe_mxfp4_workspace_region(None, 0, ctypes.byref(off), ctypes.byref(nb)) == 1
+    assert b"plan is null" in lib.moe_mxfp4_last_error()
+
+
+# ------------------------------------------------------------ binding argument checks (no device needed)
+def _unbuilt_plan(**kw):
+    """A Plan object with a configuration and a CPU workspace but no library
+    plan behind it: enough for the binding's argument checks, which raise
+    before any library call."""
+    import torch
+    p = object.__new__(moe.Plan)
+    p.cfg = cfg(hidden=256, intermediate=128, num_experts=8, top_k=2, max_tokens=16, **kw)
+    p.workspace = torch.zeros(1024, dtype=torch.uint8)
+    p._h = ctypes.c_void_p()
+    return p
+
+
+def _good_args(T=4):
+    import torch
+    return dict(hidden=torch.zeros((T, 256), dtype=torch.bfloat16), topk_ids=torch.zeros((T, 2), dtype=torch.int32),
+                topk_weights=torch.zeros((T, 2), dtype=torch.float32))
+
+
+def _bad(**changes):
+    import torch
+    a = _good_args()
+    a.update(changes)
+    return a
+
+
+@pytest.mark.parametrize("name,kw,needle", [
+    ("int64 ids", lambda t: _bad(topk_ids=torch.zeros((4, 2), dtype=torch.int64)), "topk_ids must be torch.int32"),
+    ("ids too few rows", lambda t: _bad(topk_ids=torch.zeros((3, 2), dtype=torch.int32)), "at least 4 rows"),
+    ("ids wrong k", lambda t: _bad(topk_ids=torch.zeros((4, 3), dtype=torch.int32)), "2 columns"),
+    ("fp16 weights", lambda t: _bad(topk_weights=torch.zeros((4, 2), dtype=torch.float16)), "topk_weights must be"),
+    ("weights short", lambda t: _bad(topk_weights=torch.zeros((2, 2), dtype=torch.float32)), "at least 4 rows"),
+    ("fp32 hidden", lambda t: _bad(hidden=torch.zeros((4, 256), dtype=torch.float32)), "hidden must be torch.bfloat16"),
+    ("hidden width", lambda t: _bad(hidden=torch.zeros((4, 128), dtype=torch.bfloat16)), "256 columns"),
+    ("strided hidden", lambda t: _bad(hidden=torch.zeros((4, 512), dtype=torch.bfloat16)[:, ::2]), "contiguous"),
+    ("out short", lambda t: _bad(out=torch.zeros((2, 256), dtype=torch.bfloat16)), "out must have at least 4 rows"),
+    ("acc dtype", lambda t: _bad(acc=torch.zeros((4, 256), dtype=torch.bfloat16)), "acc must be torch.float32"),
+    ("acc short", lambda t: _bad(acc=torch.zeros((3, 256), dtype=torch.float32)), "acc must have at least 4 rows"),
+    ("device", lambda t: _bad(topk_ids=torch.zeros((4, 2), dtype=torch.int32, device="meta")), "must be on cpu"),
+    ("tokens past hidden", lambda t: dict(_good_args(), num_tokens=5), "num_tokens must be in [0, 4]"),
+    ("negative tokens", lambda t: dict(_good_args(), num_tokens=-1), "num_tokens must be in [0, 4]"),
+    ("workspace dtype", lambda t: dict(_good_args(), workspace=torch.zeros(64, dtype=torch.int32)), "workspace must be"),
+])
+def test_binding_rejects_bad_forward_arguments(lib, name, kw, needle):
+    """int64 ids (torch.topk's default), short or mistyped tensors, strided
+    views, another device, or a token count past the rows would make the
+    kernels read or write out of bounds: the binding raises MOE_ERR_ARG first."""
+    import torch
+    p = _unbuilt_plan()
+    for fn in (p.forward, p.forward_fused):
+        with pytest.raises(moe.MoeError) as ei:
+            fn(**kw(torch))
+        assert ei.value.status == 1 and needle in ei.value.message, (name, ei.value.message)
+
+
+def test_binding_rejects_bad_route_router_and_quantiser_arguments(lib):
+    import torch
+    p = _unbuilt_plan()
+    with pytest.raises(moe.MoeError, match="topk_ids must be torch.int32"):
+        p.route(torch.zeros((4, 2), dtype=torch.int64))
+    with pytest.raises(moe.MoeError, match=r"num_tokens must be in \[0, 4\]"):
+        p.route(torch.zeros((4, 2), dtype=torch.int32), num_tokens=9)
+    with pytest.raises(moe.MoeError, match="logits must be torch.float32"):
+        moe.router_topk(torch.zeros((4, 8), dtype=torch.float64), 2)
+    with pytest.raises(moe.MoeError, match="topk_ids must have 2 columns"):
+        moe.router_topk(torch.zeros((4, 8)), 2, ids=torch.zeros((4, 3), dtype=torch.int32))
+    with pytest.raises(moe.MoeError, match="x must be torch.bfloat16"):
+        moe.mxfp8_quantize(torch.zeros((4, 64)))

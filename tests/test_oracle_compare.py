@@ -47,17 +47,3 @@ def test_nonfinite_fails_and_zero_rows_exact():
     ref = np.zeros((1, 8))
     assert check_rows(np.zeros((1, 8)), ref)["pass"]
     assert not check_rows(np.full((1, 8), 1e-30), ref)["pass"]
-
-
-def test_spread_widens_only_its_own_rows():
-    from oracle import check_rows
-    ref = np.ones((2, 64))
-    out = ref.copy()
-    out[:, 0] += 0.05                                   # rel L2 0.00625 > 4e-3 in both rows
-    assert not check_rows(out, ref)["pass"]
-    spread = np.zeros_like(ref)
-    spread[0, 0] = 0.05                                 # a legitimate requantisation step in row 0 only
-    r = check_rows(out, ref, spread=spread)
-    assert r["failing_rows"] == [1]
-    spread[1, 5] = 0.05
-    assert check_rows(out, ref, spread=spread)["pass"]

@@ -87,42 +87,71 @@ def test_roundtrip_error_bound_below_block_max():
     assert (err[ok] <= bound[ok]).all()
 
 
-# ---------------------------------------------------------------- round-trip spread
-def test_spread_zero_without_uncertainty_and_far_from_decisions():
+# ---------------------------------------------------------------- admissible requantisations
+def _codes_of(values_blocks, e):
+    """E4M3 codes of [n, 32*nb] values at block exponents e [n, nb]."""
+    n, k = values_blocks.shape
+    b = values_blocks.reshape(n, k // 32, 32)
+    return F.e4m3_encode(np.ldexp(b, -e[:, :, None])).reshape(n, k)
+
+
+def test_requant_check_without_uncertainty_takes_only_the_quantisation_of_v():
     rng = np.random.default_rng(11)
     v = rng.normal(size=(6, 64))
-    rt, sp = moe.mxfp8_roundtrip_spread(v, 0.0)
-    np.testing.assert_array_equal(rt, moe.mxfp8_roundtrip(v))
-    assert not sp.any()
-    # grid points of E4M3 under scale 2^0 with the block maximum at 500 (e = 0):
-    # every element sits on a code, a hair of uncertainty changes nothing
-    grid = np.array([F.e4m3_value(c) for c in range(1, 120)])
-    v = np.concatenate([grid[:31], [500.0]])[None, :]
-    rt, sp = moe.mxfp8_roundtrip_spread(v, 1e-12)
-    assert not sp[0, :31].any()
+    c, s = moe.mxfp8_quantize(v)
+    r = moe.mxfp8_requant_check(v, 0.0, c, s)
+    assert r["n_bad"] == 0 and r["n_differ"] == 0 and r["n_ambiguous"] == 0 and r["n"] == v.size
+    np.testing.assert_array_equal(r["values"], moe.mxfp8_roundtrip(v))
+    c2 = c.copy()
+    c2[2, 7] = c2[2, 7] + 1 if (c2[2, 7] & 0x7F) < 0x7E else c2[2, 7] - 1   # one code step off
+    r = moe.mxfp8_requant_check(v, 0.0, c2, s)
+    assert r["n_bad"] == 1 and not r["admissible"][2, 7]
+    s2 = s.copy()
+    s2[4, 1] += 1                                     # another block exponent: all 32 elements wrong
+    assert moe.mxfp8_requant_check(v, 0.0, c, s2)["n_bad"] == 32
 
 
-def test_spread_at_a_rounding_midpoint_is_one_code_step():
+def test_requant_check_at_a_rounding_midpoint_takes_either_neighbour():
     # block maximum 600 -> e = 0; 1.0625 is halfway between the codes 1.0 and
-    # 1.125: round-to-nearest-even gives 1.0, an upward nudge gives 1.125
+    # 1.125: an interval around it admits both, and nothing further
     v = np.array([[1.0625] + [0.5] * 30 + [600.0]])
-    rt, sp = moe.mxfp8_roundtrip_spread(v, 1e-9)
-    assert rt[0, 0] == 1.0 and sp[0, 0] == 0.125
-    assert sp[0, 1] == 0.0
+    c, s = moe.mxfp8_quantize(v)
+    assert F.e4m3_value(c[0, 0]) == 1.0
+    r = moe.mxfp8_requant_check(v, 1e-9, c, s)
+    assert r["n_bad"] == 0 and r["n_ambiguous"] == 1 and r["ambiguous"][0, 0] and r["n_differ"] == 0
+    up = c.copy()
+    up[0, 0] += 1                                     # 1.125
+    r = moe.mxfp8_requant_check(v, 1e-9, up, s)
+    assert r["n_bad"] == 0 and r["n_differ"] == 1 and r["values"][0, 0] == 1.125
+    up[0, 0] += 1                                     # 1.25: two steps, not a correct rounding
+    assert moe.mxfp8_requant_check(v, 1e-9, up, s)["n_bad"] == 1
+    up = c.copy()
+    up[0, 1] += 1                                     # 0.5 sits on a code: no neighbour is correct
+    assert moe.mxfp8_requant_check(v, 1e-9, up, s)["n_bad"] == 1
 
 
-def test_spread_at_a_scale_boundary_covers_the_halved_block_max():
-    # block maximum exactly 448 -> e = 0 and it is exact; just below, e = -1 and
-    # the literal rule saturates it to 448 * 2^-1 = 224
+def test_requant_check_at_a_scale_boundary_takes_either_exponent():
+    # block maximum exactly 448 -> e = 0; just below it e = -1, where the
+    # literal rule saturates it to 448 * 2^-1 = 224 and 3.0 is still a code
     v = np.array([[448.0] + [3.0] * 31])
-    rt, sp = moe.mxfp8_roundtrip_spread(v, 1e-9)
-    assert rt[0, 0] == 448.0 and sp[0, 0] == 224.0
-    below = moe.mxfp8_roundtrip(np.array([[np.nextafter(448.0, 0)] + [3.0] * 31]))
-    assert below[0, 0] == 224.0
-    assert sp[0, 1] == 0.0          # 3.0 is a code at both exponents
+    c, s = moe.mxfp8_quantize(v)
+    assert s[0, 0] == 127
+    r = moe.mxfp8_requant_check(v, 1e-9, c, s)
+    assert r["n_bad"] == 0 and r["n_ambiguous"] == 32
+    e_low = np.array([[-1]])
+    c_low = _codes_of(np.nextafter(v, 0), e_low)
+    r = moe.mxfp8_requant_check(v, 1e-9, c_low, np.array([[126]], np.uint8))
+    assert r["n_bad"] == 0 and r["values"][0, 0] == 224.0 and r["values"][0, 1] == 3.0
+    assert r["n_differ"] == 1
+    # a third exponent is not reachable
+    c_2 = _codes_of(v, np.array([[-2]]))
+    assert moe.mxfp8_requant_check(v, 1e-9, c_2, np.array([[125]], np.uint8))["n_bad"] == 32
 
 
-def test_spread_bounds_every_perturbation_brute_force():
+def test_requant_check_admits_every_quantisation_inside_the_interval_brute_force():
+    """Quantise random points v' of [v - dv, v + dv] (and its ends) with the
+    oracle's own quantiser: each one is admissible; a code moved by two steps
+    where the element is not ambiguous is not."""
     rng = np.random.default_rng(12)
     for trial in range(40):
         v = rng.normal(size=(2, 64)) * np.ldexp(1.0, int(rng.integers(-8, 8)))
@@ -130,25 +159,59 @@ def test_spread_bounds_every_perturbation_brute_force():
         v[0, 3] = 1.0625 * np.ldexp(1.0, moe.mxfp8_scale_exponent(np.abs(v[0, :32]).max()))
         v[1, 40] = 448.0 * np.ldexp(1.0, int(rng.integers(-6, 3)))
         dv = np.abs(v) * 10.0 ** rng.uniform(-9, -3)
-        rt, sp = moe.mxfp8_roundtrip_spread(v, dv)
-        for _ in range(30):
-            vp = v + dv * rng.uniform(-1, 1, size=v.shape)
-            assert (np.abs(moe.mxfp8_roundtrip(vp) - rt) <= sp).all()
-        for sign in (-1.0, 1.0):     # the interval's ends
-            assert (np.abs(moe.mxfp8_roundtrip(v + sign * dv) - rt) <= sp).all()
+        for j in range(32):
+            vp = v + dv * (rng.uniform(-1, 1, size=v.shape) if j > 1 else (2 * j - 1))
+            c, s = moe.mxfp8_quantize(vp)
+            r = moe.mxfp8_requant_check(v, dv, c, s)
+            assert r["n_bad"] == 0, (trial, j)
+            assert (r["ambiguous"] | (r["values"] == r["rt"])).all()
+        c, s = moe.mxfp8_quantize(v)
+        r = moe.mxfp8_requant_check(v, dv, c, s)
+        plain = np.argwhere(~r["ambiguous"] & (np.abs(F.e4m3_value(c)) > 1) & (np.abs(F.e4m3_value(c)) < 200))
+        i, k = plain[0]
+        c2 = c.copy()
+        c2[i, k] += 2
+        assert moe.mxfp8_requant_check(v, dv, c2, s)["n_bad"] == 1
 
 
-def test_forward_spread_zero_for_bf16_and_acc_unchanged():
+def test_forward_with_its_own_requantisation_is_the_forward():
     import workloads as W
-    for act in ("bf16", "mxfp8"):
-        case = W.make_case("sp", W.LayerShape(6, 256, 128, 3, 3, 2), 13, act=act)
-        args = (case.hidden_bits, case.topk_ids, case.topk_weights, case.experts(), 3)
-        acc = moe.forward(*args, act=act)
-        acc2, bound = moe.forward(*args, act=act, with_spread=True)
-        np.testing.assert_array_equal(acc, acc2)
-        assert (bound >= 0).all()
-        if act == "bf16":
-            assert not bound.any()
+    case = W.make_case("hq", W.LayerShape(6, 256, 128, 3, 3, 2), 13, act="mxfp8")
+    args = (case.hidden_bits, case.topk_ids, case.topk_weights, case.experts(), 3)
+    acc = moe.forward(*args, act="mxfp8")
+    seen = []
+
+    def own(e, routes, h, dh):
+        seen.extend(routes)
+        assert (dh > 0).all() and dh.shape == h.shape
+        c, s = moe.mxfp8_quantize(h)
+        r = moe.mxfp8_requant_check(h, dh, c, s)
+        assert r["n_bad"] == 0 and r["n_differ"] == 0
+        return r["values"]
+
+    np.testing.assert_array_equal(moe.forward(*args, act="mxfp8", h_requant=own), acc)
+    ids = case.topk_ids
+    assert sorted(seen) == sorted((t, s) for t in range(6) for s in range(2) if 0 <= ids[t, s] < 3)
+
+
+def test_h_uncertainty_covers_an_fp32_evaluation():
+    """g and u as float32 dot products summed in 128-element blocks, silu and
+    the product in float32: h stays within h_uncertainty of the exact h."""
+    rng = np.random.default_rng(15)
+    for k in (256, 2048, 7168):
+        x = rng.normal(size=(16, k)).astype(np.float32)
+        w13 = (rng.normal(size=(64, k)) * 0.05).astype(np.float32)
+        x64, w64 = x.astype(np.float64), w13.astype(np.float64)
+        gu = x64 @ w64.T
+        g, u = gu[:, :32], gu[:, 32:]
+        h = moe.silu(g) * u
+        dh = moe.h_uncertainty(x64, w64, g, u, h)
+        acc = np.zeros((16, 64), np.float32)
+        for b in range(0, k, 128):
+            acc = (acc + x[:, b:b + 128] @ w13[:, b:b + 128].T).astype(np.float32)
+        g32, u32 = acc[:, :32], acc[:, 32:]
+        h32 = (g32 / (np.float32(1) + np.exp(-g32))) * u32
+        assert (np.abs(h32.astype(np.float64) - h) <= dh).all()
 
 
 def test_fp32_dot_bound_covers_fp32_evaluation():
