@@ -179,16 +179,63 @@ def fp32_dot_bound(k: int) -> float:
     return 2.0 * (7 + -(-k // 128) + 4) * FP32_EPS
 
 
+def _sigmoid(z):
+    """1 / (1 + e^-z) without overflow and with full relative accuracy in both tails."""
+    z = np.asarray(z, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        ez = np.exp(-np.abs(z))
+    return np.where(z >= 0, 1.0 / (1.0 + ez), ez / (1.0 + ez))
+
+
+def silu_prime(z):
+    """d/dz [z sigma(z)] = sigma(z) (1 + z sigma(-z))."""
+    z = np.asarray(z, dtype=np.float64)
+    return _sigmoid(z) * (1.0 + z * _sigmoid(-z))
+
+
+# silu'' = sigma' (2 + z (1 - 2 sigma)) vanishes at z = +-2.39935728...: the
+# positive root of 2 + z tanh(-z / 2) = 0 (Newton from 2.4 to fp64 precision).
+def _silu_prime_crit() -> float:
+    z = 2.4
+    for _ in range(60):
+        f = 2.0 - z * np.tanh(0.5 * z)
+        df = -np.tanh(0.5 * z) - 0.5 * z / np.cosh(0.5 * z) ** 2
+        z -= f / df
+    return float(z)
+
+
+SILU_PRIME_CRIT = _silu_prime_crit()
+
+
 def h_uncertainty(x_rows: np.ndarray, w13: np.ndarray, g: np.ndarray, u: np.ndarray, h: np.ndarray) -> np.ndarray:
     """Bound on |h_fp32 - h| for an fp32 evaluation of h = silu(g) * u whose
-    g and u are fp32 dot products (``fp32_dot_bound``): |silu'| <= 1.1, so
-    |dh| <= 1.1 dg (|u| + du) + |silu(g)| du, plus a few fp32 roundings of
-    silu and the product."""
+    g and u are fp32 dot products (``fp32_dot_bound``: |dg|, |du| <= gamma *
+    sum|terms|) and whose silu runs on the hardware exponential.
+
+    * g enters through silu: |silu(g') - silu(g)| <= dg * max|silu'| over
+      [g - dg, g + dg] (mean value theorem).  |silu'| is monotone between the
+      critical points of silu' (z = -c and z = c, c = 2.3994...), so its
+      maximum on the interval is at an end or at a critical point inside.
+      (The global bound |silu'| <= 1.1 would be far too loose where g << 0,
+      where silu(g) ~ g e^g is tiny and flat.)
+    * |silu(g') u' - silu(g) u| <= that * (|u| + du) + |silu(g)| du.
+    * fp32 silu(z) = z * rcp(1 + exp(-z)) with exp(-z) = 2^(-z log2 e): the
+      rounding of the exponent argument makes the exponential's relative error
+      up to about 1.5 |z| ulp, plus the unit's own, the addition, the
+      reciprocal and two products: (2 |z| + 10) ulp of h, taken generously.
+    * g < -80: exp(-g) overflows fp32 and silu comes out as -0, so h is
+      known only up to its own size there.
+    """
     inter = g.shape[1]
     gam = fp32_dot_bound(x_rows.shape[1])
     absum = np.abs(x_rows) @ np.abs(w13).T            # sum of |terms| of every dot product
     dg, du = gam * absum[:, :inter], gam * absum[:, inter:]
-    return 1.1 * dg * (np.abs(u) + du) + np.abs(silu(g)) * du + 8 * FP32_EPS * np.abs(h)
+    lo, hi = g - dg, g + dg
+    dsilu = np.maximum(np.abs(silu_prime(lo)), np.abs(silu_prime(hi)))
+    for c in (-SILU_PRIME_CRIT, SILU_PRIME_CRIT):
+        dsilu = np.where((lo <= c) & (c <= hi), np.maximum(dsilu, abs(silu_prime(np.float64(c)))), dsilu)
+    dh = dsilu * dg * (np.abs(u) + du) + np.abs(silu(g)) * du + (2.0 * np.abs(g) + 10.0) * FP32_EPS * np.abs(h)
+    return np.where(g < -80.0, dh + np.abs(h), dh)
 
 
 # --------------------------------------------------------------------------- forward
