@@ -211,6 +211,43 @@ moe_status moe_router_topk(const float* logits, int32_t num_tokens, int32_t num_
                            int32_t top_k, int32_t* topk_ids, float* topk_weights,
                            hipStream_t stream);
 
+/* Peak micro-benchmarks: the measured ceilings a benchmark reports its
+ * kernels against beside the published peaks (the pages record each run's
+ * GPU operating state because the clock policy moved their numbers: b12x PR
+ * #339, maintenance-window and extent-benchmark commits).  Not part of the
+ * layer.  `sink` is device memory of at least `grid` floats (one per
+ * workgroup; the values mean nothing); 1 <= grid <= 16384.  Enqueue-only. */
+typedef enum {
+  MOE_PROBE_READ = 0,      /* grid-stride 128-bit loads over src[bytes] */
+  MOE_PROBE_READ_NT = 1,   /* the same with non-temporal loads */
+  MOE_PROBE_COPY = 2       /* dst[bytes] = src[bytes] in 128-bit words */
+} moe_probe_memory_kind;
+/* bytes a multiple of 16; src (and dst for a copy) 16-byte aligned. */
+moe_status moe_probe_memory(int32_t kind, const void* src, void* dst, size_t bytes, float* sink, int32_t grid,
+                            hipStream_t stream);
+
+typedef enum {
+  MOE_PROBE_MFMA_BF16 = 0,   /* independent chains of v_mfma_f32_32x32x16_bf16 */
+  MOE_PROBE_MFMA_F8F4 = 1    /* v_mfma_scale_f32_16x16x128_f8f6f4, E4M3 A x E2M1 B */
+} moe_probe_mfma_kind;
+/* `iters` >= 1 rounds of eight independent MFMAs per wave, 256-thread
+ * workgroups; *flops receives the launch's multiply-add work (2 per MAC). */
+moe_status moe_probe_mfma(int32_t kind, int32_t iters, float* sink, int32_t grid, double* flops,
+                          hipStream_t stream);
+
+/* One v_mfma_scale_f32_16x16x128_f8f6f4 (E4M3 A, E2M1 B, one E8M0 scale per
+ * 32 K of each) per problem, on operands given in the instruction's lane
+ * order: a measurement of how the matrix core sums a block of 128 products,
+ * which bounds how far the MXFP8 path's fp32 h may sit from the exact h.
+ *   a_lanes  [n][64][32] u8  lane l: A row l%16, K 16q..16q+15 then 64+16q.., q = l/16
+ *   b_lanes  [n][64][16] u8  lane l: B row l%16, E2M1 K 32q..32q+31, element 2j in bits 3:0
+ *   a_scales, b_scales [n][64] u8  lane l: the scale of its row's K group q
+ *   c, d     [n][64][4] fp32 lane l: accumulator rows 4q..4q+3 of column l%16
+ * 1 <= n <= 65536; device pointers, 16-byte aligned; enqueue-only. */
+moe_status moe_probe_mfma_f8f4_blocks(const uint8_t* a_lanes, const uint8_t* b_lanes, const uint8_t* a_scales,
+                                      const uint8_t* b_scales, const float* c, float* d, int32_t n,
+                                      hipStream_t stream);
+
 /* Record one event at each stage boundary of subsequent forward calls of this
  * plan: events[0] before the first kernel, then after route, FC1, FC2 and the
  * combine (n = 5).  Pass n = 0 to stop.  The events are owned by the caller

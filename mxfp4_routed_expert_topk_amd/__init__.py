@@ -14,6 +14,8 @@ Names follow the C ABI in include/moe_mxfp4.h:
   Plan.workspace_region(region)         -> the workspace bytes of an intermediate (MXFP8 h)
   mxfp8_quantize(x_bf16)                -> (codes, scales)
   router_topk(logits, k)                -> (topk_ids, topk_weights)  (moe_router_topk)
+  probe_memory(kind, src, dst, sink)    peak micro-benchmarks (moe_probe_memory / moe_probe_mfma)
+  probe_mfma(kind, iters, sink)         -> flops of the launch
 """
 from __future__ import annotations
 
@@ -34,7 +36,9 @@ MOE_WS_H_CODES = 0
 MOE_WS_H_SCALES = 1
 EXPORTS = ("moe_mxfp4_query_sizes", "moe_mxfp4_plan", "moe_mxfp4_forward", "moe_mxfp4_forward_fused",
            "moe_mxfp4_fused_status", "moe_mxfp4_route", "moe_mxfp4_workspace_region", "moe_mxfp8_quantize",
-           "moe_router_topk", "moe_mxfp4_set_stage_events", "moe_mxfp4_destroy", "moe_mxfp4_last_error")
+           "moe_router_topk", "moe_probe_memory", "moe_probe_mfma", "moe_probe_mfma_f8f4_blocks",
+           "moe_mxfp4_set_stage_events",
+           "moe_mxfp4_destroy", "moe_mxfp4_last_error")
 _STATUS_FNS = tuple(n for n in EXPORTS if n not in ("moe_mxfp4_destroy", "moe_mxfp4_last_error"))
 
 
@@ -86,6 +90,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_mxfp4_workspace_region.argtypes = [vp, i32, ctypes.POINTER(sz), ctypes.POINTER(sz)]
     lib.moe_mxfp8_quantize.argtypes = [vp, i32, i32, vp, vp, vp]
     lib.moe_router_topk.argtypes = [vp, i32, i32, i32, vp, vp, vp]
+    lib.moe_probe_memory.argtypes = [i32, vp, vp, sz, vp, i32, vp]
+    lib.moe_probe_mfma.argtypes = [i32, i32, vp, i32, ctypes.POINTER(ctypes.c_double), vp]
+    lib.moe_probe_mfma_f8f4_blocks.argtypes = [vp, vp, vp, vp, vp, vp, i32, vp]
     lib.moe_mxfp4_set_stage_events.argtypes = [vp, ctypes.POINTER(vp), i32]
     lib.moe_mxfp4_destroy.argtypes = [vp]
     lib.moe_mxfp4_destroy.restype = None
@@ -293,3 +300,40 @@ def mxfp8_quantize(x_bf16, stream=None):
     scales = torch.empty((rows, max(cols // 32, 0)), dtype=torch.uint8, device=x_bf16.device)
     _check(load_library().moe_mxfp8_quantize(_ptr(x_bf16), rows, cols, _ptr(codes), _ptr(scales), _stream(stream)))
     return codes, scales
+
+
+MOE_PROBE_READ, MOE_PROBE_READ_NT, MOE_PROBE_COPY = 0, 1, 2
+MOE_PROBE_MFMA_BF16, MOE_PROBE_MFMA_F8F4 = 0, 1
+
+
+def probe_memory(kind, src, dst, sink, grid, stream=None):
+    """One launch of a memory probe over src (and dst): moe_probe_memory."""
+    nbytes = src.numel() * src.element_size()
+    _check(load_library().moe_probe_memory(int(kind), _ptr(src), _ptr(dst), nbytes, _ptr(sink), int(grid),
+                                           _stream(stream)))
+
+
+def probe_mfma(kind, iters, sink, grid, stream=None):
+    """One launch of an MFMA probe: moe_probe_mfma; returns its flops."""
+    fl = ctypes.c_double()
+    _check(load_library().moe_probe_mfma(int(kind), int(iters), _ptr(sink), int(grid), ctypes.byref(fl),
+                                         _stream(stream)))
+    return fl.value
+
+
+def probe_mfma_f8f4_blocks(a_lanes, b_lanes, a_scales, b_scales, c, stream=None):
+    """d = one scaled MFMA per problem (moe_probe_mfma_f8f4_blocks); tensors in lane order."""
+    import torch
+    n = a_lanes.shape[0]
+    dev = a_lanes.device
+    _need(a_lanes, "a_lanes", torch.uint8, n, None, dev, ndim=3)
+    _need(b_lanes, "b_lanes", torch.uint8, n, None, dev, ndim=3)
+    _need(a_scales, "a_scales", torch.uint8, n, 64, dev)
+    _need(b_scales, "b_scales", torch.uint8, n, 64, dev)
+    _need(c, "c", torch.float32, n, None, dev, ndim=3)
+    if a_lanes.shape[1:] != (64, 32) or b_lanes.shape[1:] != (64, 16) or c.shape[1:] != (64, 4):
+        raise _arg_error("operands must be a [n,64,32], b [n,64,16], c [n,64,4]")
+    d = torch.empty_like(c)
+    _check(load_library().moe_probe_mfma_f8f4_blocks(_ptr(a_lanes), _ptr(b_lanes), _ptr(a_scales), _ptr(b_scales),
+                                                     _ptr(c), _ptr(d), n, _stream(stream)))
+    return d

@@ -477,6 +477,48 @@ moe_status moe_router_topk(const float* logits, int32_t T, int32_t E, int32_t k,
   return ok();
 }
 
+moe_status moe_probe_memory(int32_t kind, const void* src, void* dst, size_t bytes, float* sink, int32_t grid,
+                            hipStream_t stream) {
+  if (kind < MOE_PROBE_READ || kind > MOE_PROBE_COPY)
+    return fail(MOE_ERR_ARG, "probe kind must be 0 (read), 1 (non-temporal read) or 2 (copy), got %d", kind);
+  if (grid < 1 || grid > moe::kProbeSinkFloats)
+    return fail(MOE_ERR_ARG, "grid must be in [1, %d], got %d", moe::kProbeSinkFloats, grid);
+  if (bytes == 0 || bytes % 16) return fail(MOE_ERR_SHAPE, "bytes must be a positive multiple of 16, got %zu", bytes);
+  if (!src || !sink || (kind == MOE_PROBE_COPY && !dst)) return fail(MOE_ERR_ARG, "a probe buffer is null");
+  if (misaligned(src) || (dst && misaligned(dst)))
+    return fail(MOE_ERR_ALIGN, "probe buffers must be 16-byte aligned");
+  hipError_t e = moe::launch_probe_memory(kind, src, dst, bytes, sink, grid, stream);
+  if (e != hipSuccess) return hip_fail(e, "probe launch");
+  return ok();
+}
+
+moe_status moe_probe_mfma(int32_t kind, int32_t iters, float* sink, int32_t grid, double* flops,
+                          hipStream_t stream) {
+  if (kind != MOE_PROBE_MFMA_BF16 && kind != MOE_PROBE_MFMA_F8F4)
+    return fail(MOE_ERR_ARG, "probe kind must be 0 (bf16) or 1 (f8f6f4), got %d", kind);
+  if (grid < 1 || grid > moe::kProbeSinkFloats)
+    return fail(MOE_ERR_ARG, "grid must be in [1, %d], got %d", moe::kProbeSinkFloats, grid);
+  if (iters < 1) return fail(MOE_ERR_ARG, "iters must be >= 1, got %d", iters);
+  if (!sink || !flops) return fail(MOE_ERR_ARG, "sink and flops must not be null");
+  hipError_t e = moe::launch_probe_mfma(kind, iters, sink, grid, flops, stream);
+  if (e != hipSuccess) return hip_fail(e, "probe launch");
+  return ok();
+}
+
+moe_status moe_probe_mfma_f8f4_blocks(const uint8_t* a, const uint8_t* b, const uint8_t* sa, const uint8_t* sb,
+                                      const float* c, float* d, int32_t n, hipStream_t stream) {
+  if (n < 1 || n > 65536) return fail(MOE_ERR_ARG, "n must be in [1, 65536], got %d", n);
+  const void* ptrs[] = {a, b, sa, sb, c, d};
+  const char* names[] = {"a_lanes", "b_lanes", "a_scales", "b_scales", "c", "d"};
+  for (int i = 0; i < 6; ++i) {
+    if (!ptrs[i]) return fail(MOE_ERR_ARG, "%s is null", names[i]);
+    if (misaligned(ptrs[i])) return fail(MOE_ERR_ALIGN, "%s must be 16-byte aligned, got %p", names[i], ptrs[i]);
+  }
+  hipError_t e = moe::launch_probe_mfma_blocks(a, b, sa, sb, c, d, n, stream);
+  if (e != hipSuccess) return hip_fail(e, "probe launch");
+  return ok();
+}
+
 moe_status moe_mxfp4_set_stage_events(moe_mxfp4_plan_t p, hipEvent_t* events, int32_t n) {
   if (!p) return fail(MOE_ERR_ARG, "plan is null");
   if (n != 0 && n != 5) return fail(MOE_ERR_ARG, "stage events: n must be 0 or 5, got %d", n);

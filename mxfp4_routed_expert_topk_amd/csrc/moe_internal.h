@@ -151,6 +151,15 @@ constexpr int kRouterMaxExperts = 1024;
 hipError_t launch_router_topk(const float* logits, int32_t T, int32_t E, int32_t k, int32_t* ids, float* weights,
                               hipStream_t stream);
 
+// Peak micro-benchmarks (probe.hip).  `sink` holds one float per workgroup
+// (grid <= kProbeSinkFloats).
+constexpr int kProbeSinkFloats = 16384;
+hipError_t launch_probe_memory(int kind, const void* src, void* dst, size_t bytes, float* sink, int grid,
+                               hipStream_t stream);
+hipError_t launch_probe_mfma(int kind, int iters, float* sink, int grid, double* flops, hipStream_t stream);
+hipError_t launch_probe_mfma_blocks(const uint8_t* a, const uint8_t* b, const uint8_t* sa, const uint8_t* sb,
+                                    const float* c, float* d, int n, hipStream_t stream);
+
 hipError_t launch_combine(const float* y, const int32_t* rowpos, const int32_t* ids,
                           const float* w, int32_t T, int32_t k, int32_t H, int32_t E,
                           float* acc, uint16_t* out, hipStream_t stream);

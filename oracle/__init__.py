@@ -26,7 +26,7 @@ from .formats import (E2M1_MAGNITUDES, E4M3_MAX, bf16_bits_to_f64, dequant_mxfp4
 from .route import route_sort, route_sort_by_key
 from .router import router_topk, router_topk_np
 from .moe import (expert_mlp, forward, fp32_dot_bound, mxfp8_dequantize, mxfp8_quantize, silu_prime,
-                  mxfp8_requant_check, mxfp8_roundtrip, mxfp8_scale_exponent, silu, h_uncertainty)
+                  mxfp8_requant_check, mxfp8_quantum, mxfp8_roundtrip, mxfp8_scale_exponent, silu, h_uncertainty)
 from .compare import check_rows, rel_l2
 from .brute import forward_brute, e2m1_closed_form
 

@@ -77,8 +77,19 @@ def reference(case, tokens=None, ew=None, h_requant=None):
 def device_h_requant(case, plan, stats, workspace=None):
     """oracle.forward's h_requant hook: the device's MXFP8 h of each route (row
     rowpos[t*k+s] of the workspace regions, rowpos from the oracle's route
-    sort), checked element by element by oracle.mxfp8_requant_check; the
-    counts go to `stats`."""
+    sort), checked element by element, the counts going to `stats`:
+      n_ambiguous  codes the oracle cannot fix from an fp32 evaluation of h
+                   (oracle.h_uncertainty: the exact h lies within an fp32
+                   dot product's rounding of a rounding or scale decision);
+      n_differ     device codes other than the oracle's MXFP8 of the exact h;
+      n_beyond_fp32  of those, codes outside the fp32 band: the scaled MFMA sums
+                   a 128-product block with fewer bits than fp32 (measured by
+                   test_scaled_mfma_block_summation), so h lands on the other
+                   side of a decision a little more often;
+      n_bad        codes more than one E4M3 step from the exact h (at the
+                   device's block scale) -- none is allowed.
+    The layer is then evaluated from the device's codes, which equal the
+    oracle's everywhere else."""
     s = case.shape
     rows_all = plan.cfg.max_tokens * s.top_k
     hq = plan.workspace_region(moe.MOE_WS_H_CODES, workspace).view(rows_all, s.inter).cpu().numpy()
@@ -88,11 +99,20 @@ def device_h_requant(case, plan, stats, workspace=None):
 
     def take(e, routes, h, dh):
         rows = [int(rowpos[t * s.top_k + sl]) for t, sl in routes]
-        r = oracle.mxfp8_requant_check(h, dh, hq[rows], hs[rows])
+        codes, scales = hq[rows], hs[rows]
+        band = oracle.mxfp8_requant_check(h, dh, codes, scales)
+        step = oracle.mxfp8_requant_check(h, oracle.mxfp8_quantum(h), codes, scales)
         with lock:
-            for key in ("n", "n_ambiguous", "n_differ", "n_bad"):
-                stats[key] += r[key]
-        return r["values"]
+            stats["n"] += band["n"]
+            stats["n_ambiguous"] += band["n_ambiguous"]
+            stats["n_differ"] += int((step["values"] != band["rt"]).sum())
+            stats["n_beyond_fp32"] += band["n_bad"]
+            stats["n_bad"] += step["n_bad"]
+            for i, c in np.argwhere(~step["admissible"])[:4]:
+                say(f"  wrong h code: expert {e} route {routes[i]} column {c}: exact h {h[i, c]!r}, "
+                    f"oracle {band['rt'][i, c]!r}, device {step['values'][i, c]!r}, device scale byte "
+                    f"{int(scales[i, c // 32])}")
+        return step["values"]
     return take
 
 
@@ -104,13 +124,15 @@ def check_layer(case, out, acc, tokens=None, ew=None, plan=None, workspace=None)
     hook = None
     if case.act == "mxfp8":
         assert plan is not None, "the MXFP8 check reads the forward's h from the plan's workspace"
-        stats = dict(n=0, n_ambiguous=0, n_differ=0, n_bad=0)
+        stats = dict(n=0, n_ambiguous=0, n_differ=0, n_beyond_fp32=0, n_bad=0)
         hook = device_h_requant(case, plan, stats, workspace)
     ref = reference(case, sel, ew, hook)
     if stats is not None:
-        say(f"  h codes: {stats['n']} checked, {stats['n_ambiguous']} ambiguous, "
-            f"{stats['n_differ']} taken the other correct way, {stats['n_bad']} wrong")
-        assert stats["n_bad"] == 0, f"{case.name}: {stats['n_bad']} requantised h codes are not a correct MXFP8 of h"
+        say(f"  h codes: {stats['n']} checked, {stats['n_ambiguous']} ambiguous under fp32 rounding, "
+            f"{stats['n_differ']} differ from the oracle's ({stats['n_beyond_fp32']} beyond fp32 rounding), "
+            f"{stats['n_bad']} more than one step off")
+        assert stats["n_bad"] == 0, f"{case.name}: {stats['n_bad']} requantised h codes are off by more than a step"
+        assert stats["n_differ"] <= 1e-3 * stats["n"], f"{case.name}: {stats}"
     out_bits = G.bf16_bits(out)[sel]
     out_v = oracle.bf16_bits_to_f64(out_bits)
     r_out = oracle.check_rows(out_v, ref)
@@ -598,7 +620,7 @@ def test_negative_control_swapped_nibbles_fail_the_check(act, T):
     plan, _ = G.make_plan(case, weights=[_swap_nibbles(w[0]), w[1], _swap_nibbles(w[2]), w[3]])
     out, acc = G.run_forward(plan, case)
     assert torch.isfinite(acc).all()
-    stats = dict(n=0, n_ambiguous=0, n_differ=0, n_bad=0)
+    stats = dict(n=0, n_ambiguous=0, n_differ=0, n_beyond_fp32=0, n_bad=0)
     hook = device_h_requant(case, plan, stats) if act == "mxfp8" else None
     ref = reference(case, h_requant=hook)
     rl2 = [oracle.rel_l2(a, b) for a, b in zip(acc.cpu().numpy(), ref) if np.linalg.norm(b) > 0]
@@ -708,6 +730,80 @@ def test_scale_byte_validation(byte, act, bad):
         assert f"0x{byte:02X}" in ei.value.message and "expert 2, row 100, group 1" in ei.value.message
     else:
         moe.Plan(cfg, *w)
+
+
+# ------------------------------------------------------------------ how the scaled MFMA sums a block
+def _mfma_blocks(rng, n, one_binade, c_scale):
+    """Random problems for moe_probe_mfma_f8f4_blocks: logical A [n,16,128]
+    E4M3 codes, B [n,16,128] E2M1 codes, scales [n,16,4], C [n,16,16]; returns
+    the lane-order tensors and the exact fp64 D."""
+    if one_binade:
+        a = (0x38 | rng.integers(0, 8, (n, 16, 128)) | (rng.integers(0, 2, (n, 16, 128)) << 7)).astype(np.uint8)
+        b = (rng.integers(2, 4, (n, 16, 128)) | (rng.integers(0, 2, (n, 16, 128)) << 3)).astype(np.uint8)
+        sa = np.full((n, 16, 4), 127, np.uint8)
+        sb = np.full((n, 16, 4), 127, np.uint8)
+    else:
+        a = rng.integers(0, 256, (n, 16, 128)).astype(np.uint8)
+        a[(a & 0x7F) == 0x7F] = 0x38                       # no NaN codes
+        b = rng.integers(0, 16, (n, 16, 128)).astype(np.uint8)
+        sa = rng.integers(120, 135, (n, 16, 4)).astype(np.uint8)
+        sb = rng.integers(120, 131, (n, 16, 4)).astype(np.uint8)
+    c = (rng.uniform(-1, 1, (n, 16, 16)) * c_scale).astype(np.float32)
+    av = oracle.e4m3_value(a) * np.repeat(oracle.e8m0_value(sa), 32, axis=2)
+    bv = oracle.e2m1_value(b) * np.repeat(oracle.e8m0_value(sb), 32, axis=2)
+    prods = av[:, :, None, :] * bv[:, None, :, :]             # [n, m, n', k]
+    exact = c.astype(np.float64) + prods.sum(axis=3)
+    maxterm = np.maximum(np.abs(prods).max(axis=3), np.abs(c))
+    # lane order: lane l = 16q + r holds A row r bytes K 16q.. and 64+16q.., B row r K 32q..32q+31
+    lanes_a = np.empty((n, 64, 32), np.uint8)
+    lanes_b = np.empty((n, 64, 16), np.uint8)
+    lanes_sa = np.empty((n, 64), np.uint8)
+    lanes_sb = np.empty((n, 64), np.uint8)
+    lanes_c = np.empty((n, 64, 4), np.float32)
+    for q in range(4):
+        for r in range(16):
+            l = 16 * q + r
+            lanes_a[:, l, :16] = a[:, r, 16 * q:16 * q + 16]
+            lanes_a[:, l, 16:] = a[:, r, 64 + 16 * q:64 + 16 * q + 16]
+            kb = b[:, r, 32 * q:32 * q + 32]
+            lanes_b[:, l] = kb[:, 0::2] | (kb[:, 1::2] << 4)
+            lanes_sa[:, l] = sa[:, r, q]
+            lanes_sb[:, l] = sb[:, r, q]
+            lanes_c[:, l] = c[:, 4 * q:4 * q + 4, r]
+    return (lanes_a, lanes_b, lanes_sa, lanes_sb, lanes_c), exact, maxterm
+
+
+def _unlane(d):
+    n = d.shape[0]
+    out = np.empty((n, 16, 16))
+    for q in range(4):
+        for r in range(16):
+            out[:, 4 * q:4 * q + 4, r] = d[:, 16 * q + r]
+    return out
+
+
+def test_scaled_mfma_block_summation():
+    """How v_mfma_scale_f32_16x16x128_f8f6f4 sums its 128 exact products: when
+    every product (and C) lies in one binade the result is the exact sum;
+    across a wide range of magnitudes it is not an fp32-rounded sum -- the
+    small products lose their low bits against the largest -- but the error
+    stays under 2^-10 of the largest term.  This is why the MXFP8 check allows
+    h codes one E4M3 step off beyond fp32 rounding."""
+    rng = np.random.default_rng(17)
+    for one_binade, c_scale in ((True, 0.0), (False, 0.0), (False, 64.0)):
+        lanes, exact, maxterm = _mfma_blocks(rng, 512, one_binade, c_scale)
+        d = moe.probe_mfma_f8f4_blocks(*(G.to_dev(t) for t in lanes))
+        torch.cuda.synchronize()
+        got = _unlane(d.cpu().numpy()).astype(np.float64)
+        err = np.abs(got - exact)
+        rel = err / np.ldexp(1.0, np.frexp(maxterm)[1])          # in units of the largest term's binade
+        say(f"  one binade={one_binade} C scale={c_scale}: exact {np.mean(err == 0):.4f}, "
+            f"max err {rel.max():.3e} of the largest term's binade")
+        if one_binade:
+            assert (err == 0).all()
+        else:
+            assert rel.max() < 2.0 ** -10
+            assert (err == 0).mean() < 0.5          # and not an fp32-exact dot product
 
 
 # ------------------------------------------------------------------ MXFP8 activation quantiser

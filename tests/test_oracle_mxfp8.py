@@ -267,3 +267,20 @@ def test_fp32_dot_bound_covers_fp32_evaluation():
             acc = (acc + x[:, b:b + 128] @ w[b:b + 128]).astype(np.float32)
         absum = np.abs(x.astype(np.float64)) @ np.abs(w.astype(np.float64))
         assert (np.abs(acc - exact) <= moe.fp32_dot_bound(k) * absum).all()
+
+
+def test_quantum_is_the_e4m3_grid_spacing():
+    """mxfp8_quantum against the distance between neighbouring E4M3 values of
+    every code at exponent 0 (block maximum 448 fixes e = 0)."""
+    vals = np.array([F.e4m3_value(c) for c in range(0, 0x7F)])
+    for c in range(0, 0x7E):
+        v = np.zeros((1, 32))
+        v[0, 0] = 448.0
+        v[0, 1] = vals[c]
+        assert moe.mxfp8_quantum(v)[0, 1] == vals[c + 1] - vals[c], c
+    # a value one quantum away from a code always quantises to that code or a neighbour
+    rng = np.random.default_rng(16)
+    v = rng.normal(size=(8, 64)) * 3
+    c, s = moe.mxfp8_quantize(v)
+    r = moe.mxfp8_requant_check(v, moe.mxfp8_quantum(v), c, s)
+    assert r["n_bad"] == 0 and r["n_ambiguous"] > 0.9 * v.size
