@@ -1,35 +1,45 @@
 """Benchmark of the MXFP4 routed-expert MoE layer on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--m 128] [--no-extra] [--no-cpu]
-                    [--workload decode|prefill1536|fusedsum4096|mxfp8x4096]
+                    [--workload decode|prefill1536|fusedsum4096|mxfp8x4096] [--fused]
 
-A step is one moe_mxfp4_forward call (route -> FC1 -> FC2 -> combine) over one
-batch of the decode workload: hidden 7168, intermediate 2048, 224 resident of
-384 experts, top-8, MXFP4 weights (E8M0 scales in [120,130]), bf16 activations
-N(0,1), route ids uniform over 0..383 (ids >= 224 contribute an exact zero),
-M tokens (default 128).  Inputs are resident in HBM before timing.  Eight
-routing/activation sets are rotated so consecutive steps touch different
-experts (small-M working sets would otherwise stay in the 256 MB last-level
-cache between steps).
+A step is one moe_mxfp4_forward call (the whole layer: route -> FC1 -> FC2 ->
+weighted sum) over one batch of the decode workload: hidden 7168, intermediate
+2048, 224 resident of 384 experts, top-8, MXFP4 weights (E8M0 scales in
+[120,130]), bf16 activations N(0,1), route ids uniform over 0..383 (ids >= 224
+contribute an exact zero), M tokens (default 128).  Inputs are resident in HBM
+before timing.  Eight routing/activation sets are rotated so consecutive steps
+touch different experts (small-M working sets would otherwise stay in the
+256 MB last-level cache between steps).
 
 --workload picks a single prefill configuration instead (1536 tokens uniform,
 4096 tokens Zipf fused-sum, 4096 tokens MXFP8), for profiling one workload at a
 time: its tokens/s is the value and its FC1 kernel is priced against the MFMA
 peak of its dtype (extras and the CPU baseline are skipped).
 
-Prints ONE JSON line: whole-job tokens/s (`value`, eager launches; the same
-steps replayed from captured hipGraphs are reported beside it); the roofline of the
-dominant kernel (FC1), timed with HIP events recorded on the launch stream
-right before and after that kernel in a second pass over the same steps; the layer's own
-HBM fraction; extra entries for the other decode batch sizes and the prefill
-workloads (unless --no-extra); the fp64 CPU oracle timed on a bounded sample
-(unless --no-cpu).
+Prints ONE JSON line:
+ * `value`: whole-job tokens/s of K back-to-back eager steps (one event pair);
+ * `layer`: per-step event pairs -- median and p90 with warm caches, and again
+   with a 1 GiB write between steps (cold: nothing of the last step is left in
+   the caches) -- the same steps replayed from captured hipGraphs, per-stage
+   times, and a SHA-256 prefix of the output (input set 0);
+ * `roofline`: the dominant kernel (FC1) timed by HIP events recorded on its
+   launch stream, priced against the published peak and against the ceiling
+   measured on the same box (`ceilings`: the library's peak micro-benchmarks);
+ * `gpu_state`: clocks, power and performance level before and after timing;
+ * `context`: the pages' full-model decode step figures (another machine and
+   the whole model: context only);
+ * `extra` (unless --no-extra): the other decode batch sizes, the prefill
+   workloads, the pages' K3 expert shapes and the router;
+ * `cpu_baseline` (unless --no-cpu): the fp64 CPU oracle on a bounded sample.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import subprocess
 import sys
 import time
 
@@ -43,6 +53,14 @@ BF16_PEAK_TFLOPS = 2500.0      # dense bf16 MFMA
 FP8_PEAK_TFLOPS = 5000.0       # dense fp8 MFMA
 METRIC = "MoE layer tokens/s + % HBM roofline (decode M≤128) / % MFMA peak (prefill)"
 STAGES = ("route", "fc1", "fc2", "combine")
+FLUSH_BYTES = 1 << 30
+CONTEXT = {
+    "pages_full_model_decode_step_ms": {"fused_megamoe": 43.3, "nccl_fixed_chain": 54.6},
+    "hardware": "4x GB300 (SM100), expert parallel over 4 GPUs",
+    "workload": "FP8 activations x MXFP4 experts, 93-layer K3 model, one decode stream",
+    "source": "pegainfer PR #867 (K3 model line: decode E2E at ep_size 4 with MegaMoE(situ) transport), description",
+    "note": "context only: a whole-model step on other hardware, not this layer on one MI355X",
+}
 
 
 def log(msg):
@@ -54,6 +72,73 @@ def expert_bytes(H, I):
     return (2 * I * H // 2 + 2 * I * H // 32), (H * I // 2 + H * I // 32)
 
 
+def pct(a, q):
+    return float(np.percentile(np.asarray(a), q))
+
+
+# ----------------------------------------------------------------------------- box state and ceilings
+def gpu_state():
+    """Clock levels, power and performance level of the GPU(s) as rocm-smi
+    reports them (the pages saw a clock policy move their numbers)."""
+    out = {}
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--showpower", "--showperflevel", "--json"],
+                           capture_output=True, text=True, timeout=20)
+        data = json.loads(r.stdout) if r.stdout.strip().startswith("{") else {}
+        for card, v in data.items():
+            if not isinstance(v, dict):
+                continue
+            keep = {k: v[k] for k in v if any(s in k.lower() for s in ("sclk", "mclk", "fclk", "power", "perf"))}
+            if keep:
+                out[card] = keep
+        if not out:
+            out["rocm_smi"] = (r.stdout or r.stderr).strip()[:400]
+    except Exception as e:          # the state is a record, never a reason to fail the run
+        out["error"] = repr(e)[:200]
+    return out
+
+
+def ceilings():
+    """Measured peaks on this machine with the library's micro-benchmarks: HBM
+    read (plain and non-temporal 128-bit loads over 4 GiB), copy (2 GiB each
+    way, read + write bytes), and the two MFMA instructions the prefill kernels
+    use."""
+    import torch
+    import mxfp4_routed_expert_topk_amd as moe
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    sink = torch.empty(16384, dtype=torch.float32, device="cuda")
+    res = {}
+
+    def timed(fn, reps=5):
+        fn()
+        torch.cuda.synchronize()
+        ts, r = [], None
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            r = fn()
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b) * 1e-3)
+        return min(ts), r
+
+    buf = torch.ones(4 << 30, dtype=torch.uint8, device="cuda")
+    for name, kind in (("hbm_read_gbs", moe.MOE_PROBE_READ), ("hbm_read_nt_gbs", moe.MOE_PROBE_READ_NT)):
+        t, _ = timed(lambda: moe.probe_memory(kind, buf, None, sink, cus * 8))
+        res[name] = round(buf.numel() / t / 1e9, 1)
+    src, dst = buf[: 2 << 30], buf[2 << 30:]
+    t, _ = timed(lambda: moe.probe_memory(moe.MOE_PROBE_COPY, src, dst, sink, cus * 8))
+    res["hbm_copy_gbs"] = round(2 * src.numel() / t / 1e9, 1)
+    del buf, src, dst
+    for name, kind, iters in (("mfma_bf16_tflops", moe.MOE_PROBE_MFMA_BF16, 4000),
+                              ("mfma_f8f4_tflops", moe.MOE_PROBE_MFMA_F8F4, 8000)):
+        t, fl = timed(lambda: moe.probe_mfma(kind, iters, sink, cus * 4))
+        res[name] = round(fl / t / 1e12, 1)
+    torch.cuda.empty_cache()
+    return res
+
+
+# ----------------------------------------------------------------------------- workloads
 def build_plan(cid, max_tokens):
     import torch
     import mxfp4_routed_expert_topk_amd as moe
@@ -73,26 +158,20 @@ def build_plan(cid, max_tokens):
 
 
 class Batches:
-    """`sets` device-resident input sets of one configuration at T tokens."""
+    """`sets` device-resident input sets of one workload at T tokens."""
 
     fused = False   # also time the one-launch forward (--fused)
 
-    def __init__(self, plan, cid, tokens, sets):
+    def __init__(self, plan, base, sets, make):
         import torch
-        import workloads as W
         from workloads import device as D
         self.plan = plan
-        base = W.config_case(cid, m=tokens if cid == 1 else None)
         self.base = base
         s = base.shape
         self.T, self.H, self.I, self.E, self.k = s.tokens, s.hidden, s.inter, s.experts, s.top_k
-        conf = W.CONFIGS[cid]
         self.inputs, self.touched, self.valid = [], [], []
         for j in range(sets):
-            c = base if j == 0 else W.make_case(base.name, s, base.seed + 100000 * j, routing=conf["routing"],
-                                                scale_lo=base.scale_lo, scale_hi=base.scale_hi,
-                                                invalid_frac=conf.get("invalid_frac", 0.0), act=base.act,
-                                                weight_seed=base.wseed)
+            c = base if j == 0 else make(j)
             self.inputs.append((D.to_dev(c.hidden_bits).view(torch.bfloat16), D.to_dev(c.topk_ids),
                                 D.to_dev(c.topk_weights)))
             v = c.topk_ids[(c.topk_ids >= 0) & (c.topk_ids < self.E)]
@@ -100,6 +179,24 @@ class Batches:
             self.valid.append(int(v.size))
         self.acc = torch.full((self.T, self.H), float("nan"), device="cuda") if base.nan_accumulator else None
         self.out = torch.empty((self.T, self.H), dtype=torch.bfloat16, device="cuda")
+        self.flush_buf = None
+
+    @classmethod
+    def config(cls, plan, cid, tokens, sets):
+        import workloads as W
+        base = W.config_case(cid, m=tokens if cid == 1 else None)
+        conf = W.CONFIGS[cid]
+        return cls(plan, base, sets, lambda j: W.make_case(
+            base.name, base.shape, base.seed + 100000 * j, routing=conf["routing"], scale_lo=base.scale_lo,
+            scale_hi=base.scale_hi, invalid_frac=conf.get("invalid_frac", 0.0), act=base.act,
+            weight_seed=base.wseed))
+
+    @classmethod
+    def k3(cls, plan, m, sets):
+        import workloads as W
+        base = W.k3_case(m)
+        return cls(plan, base, sets, lambda j: W.make_case(base.name, base.shape, base.seed + 100000 * j,
+                                                           routing="uniform", weight_seed=base.wseed))
 
     def per_step(self, j):
         """Algorithmic layer bytes, FC1 bytes and flops of input set j."""
@@ -110,41 +207,80 @@ class Batches:
             layer += self.T * self.H * 4
         return layer, t * w13 + self.T * self.H * 2, 6.0 * v * self.H * self.I
 
-    def _loop(self, steps, first, events=None):
-        for j in range(steps):
-            x, ids, wts = self.inputs[(first + j) % len(self.inputs)]
-            if events is not None:
-                self.plan.set_stage_events(events[j])
-            self.plan.forward(x, ids, wts, out=self.out, acc=self.acc)
+    def step(self, j):
+        x, ids, wts = self.inputs[j % len(self.inputs)]
+        self.plan.forward(x, ids, wts, out=self.out, acc=self.acc)
+
+    def _flush(self):
+        import torch
+        if self.flush_buf is None:
+            self.flush_buf = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+        self.flush_buf.fill_(1)
+
+    def per_step_times(self, steps, first, flush):
+        """One event pair per step; with `flush`, 1 GiB is written between steps
+        (outside the timed pairs)."""
+        import torch
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        torch.cuda.synchronize()
+        for j, (a, b) in enumerate(evs):
+            if flush:
+                self._flush()
+            a.record()
+            self.step(first + j)
+            b.record()
+        torch.cuda.synchronize()
+        return np.array([a.elapsed_time(b) for a, b in evs])   # ms
 
     def run(self, steps, warmup):
-        """Time `steps` forwards back to back (the headline), then the same
-        steps again with stage events recorded between the kernels (per-kernel
-        durations on the launch stream)."""
+        """The headline (back-to-back steps, one event pair), then per-step
+        pairs warm and cold, stage events (per-kernel times on the launch
+        stream), graph replay, and optionally the one-launch forward."""
         import torch
-        self._loop(warmup, 0)
+        for j in range(warmup):
+            self.step(j)
         start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         start.record()
-        self._loop(steps, warmup)
+        for j in range(steps):
+            self.step(warmup + j)
         end.record()
         torch.cuda.synchronize()
         ms = start.elapsed_time(end) / steps
+        warm = self.per_step_times(steps, warmup, False)
+        cold = self.per_step_times(steps, warmup, True)
+        self.flush_buf = None
         evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
         for e in evs:
             for ev in e:
                 ev.record()              # creates the HIP event before the timed loop
         torch.cuda.synchronize()
-        self._loop(steps, warmup, evs)
+        for j in range(steps):
+            self.plan.set_stage_events(evs[j])
+            self.step(warmup + j)
         torch.cuda.synchronize()
         self.plan.set_stage_events(None)
         stage = np.array([[e[i].elapsed_time(e[i + 1]) for i in range(4)] for e in evs])  # ms
         alg = np.array([self.per_step(warmup + j) for j in range(steps)])
-        return {"ms_per_step": ms, "ms_per_step_with_events": float(stage.sum(axis=1).mean()),
+        return {"ms_per_step": ms, "warm_ms": warm, "cold_ms": cold,
+                "ms_per_step_with_events": float(stage.sum(axis=1).mean()),
                 "stage_ms": stage.mean(axis=0), "fc1_ms": stage[:, 1],
                 "layer_bytes": alg[:, 0].mean(), "fc1_bytes": alg[:, 1].mean(), "flops": alg[:, 2].mean(),
                 "graph_ms_per_step": self.run_graph(steps, warmup),
-                "fused_ms_per_step": self.run_fused(steps, warmup) if self.fused else None}
+                "fused_ms_per_step": self.run_fused(steps, warmup) if self.fused else None,
+                "digest": self.digest()}
+
+    def digest(self):
+        """SHA-256 prefix of the outputs of input set 0 (bf16 out, and the fp32
+        accumulator where the workload keeps one): equal across runs and boxes
+        when the kernels are deterministic."""
+        import torch
+        self.step(0)
+        torch.cuda.synchronize()
+        h = hashlib.sha256(self.out.view(torch.uint8).cpu().numpy().tobytes())
+        if self.acc is not None:
+            h.update(self.acc.view(torch.uint8).cpu().numpy().tobytes())
+        return h.hexdigest()[:16]
 
     def run_fused(self, steps, warmup):
         """The same steps through the one-launch forward (bf16, at most 256
@@ -193,22 +329,30 @@ class Batches:
         del graphs
         return start.elapsed_time(end) / steps
 
-    def summary(self, r):
+    def summary(self, r, ceil=None):
         ms = r["ms_per_step"]
         gbs = r["layer_bytes"] / (ms * 1e-3) / 1e9
         tflops = r["flops"] / (ms * 1e-3) / 1e12
         peak = FP8_PEAK_TFLOPS if self.base.act == "mxfp8" else BF16_PEAK_TFLOPS
-        return {"tokens": self.T, "us_per_step": round(ms * 1e3, 2), "tokens_per_s": round(self.T / (ms * 1e-3), 1),
-                "layer_hbm_gbs": round(gbs, 1), "layer_hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
-                "tflops": round(tflops, 2), "mfma_frac": round(tflops / peak, 4),
-                "mfma_peak_tflops": peak,
-                "stage_us": {k: round(float(v) * 1e3, 2) for k, v in zip(STAGES, r["stage_ms"])},
-                "us_per_step_with_stage_events": round(r["ms_per_step_with_events"] * 1e3, 2),
-                "graph_us_per_step": round(r["graph_ms_per_step"] * 1e3, 2),
-                "graph_tokens_per_s": round(self.T / (r["graph_ms_per_step"] * 1e-3), 1),
-                **({"fused_us_per_step": round(r["fused_ms_per_step"] * 1e3, 2),
-                    "fused_tokens_per_s": round(self.T / (r["fused_ms_per_step"] * 1e-3), 1)}
-                   if r.get("fused_ms_per_step") else {})}
+        out = {"tokens": self.T, "us_per_step": round(ms * 1e3, 2), "tokens_per_s": round(self.T / (ms * 1e-3), 1),
+               "p50_us": round(pct(r["warm_ms"], 50) * 1e3, 2), "p90_us": round(pct(r["warm_ms"], 90) * 1e3, 2),
+               "cold_p50_us": round(pct(r["cold_ms"], 50) * 1e3, 2),
+               "cold_p90_us": round(pct(r["cold_ms"], 90) * 1e3, 2),
+               "layer_hbm_gbs": round(gbs, 1), "layer_hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+               "tflops": round(tflops, 2), "mfma_frac": round(tflops / peak, 4), "mfma_peak_tflops": peak,
+               "stage_us": {k: round(float(v) * 1e3, 2) for k, v in zip(STAGES, r["stage_ms"])},
+               "us_per_step_with_stage_events": round(r["ms_per_step_with_events"] * 1e3, 2),
+               "graph_us_per_step": round(r["graph_ms_per_step"] * 1e3, 2),
+               "graph_tokens_per_s": round(self.T / (r["graph_ms_per_step"] * 1e-3), 1),
+               "output_sha256_16": r["digest"]}
+        if ceil:
+            out["layer_hbm_frac_of_measured_read"] = round(gbs / ceil["hbm_read_nt_gbs"], 4)
+            key = "mfma_f8f4_tflops" if self.base.act == "mxfp8" else "mfma_bf16_tflops"
+            out["mfma_frac_of_measured"] = round(tflops / ceil[key], 4)
+        if r.get("fused_ms_per_step"):
+            out["fused_us_per_step"] = round(r["fused_ms_per_step"] * 1e3, 2)
+            out["fused_tokens_per_s"] = round(self.T / (r["fused_ms_per_step"] * 1e-3), 1)
+        return out
 
 
 # FC1 kernel source of each workload (the counter records hash it with the shared header)
@@ -218,35 +362,9 @@ PREFILL = {"prefill1536": 2, "fusedsum4096": 3, "mxfp8x4096": 4}
 
 
 def source_hash(workload):
-    import hashlib
     csrc = os.path.join(ROOT, "mxfp4_routed_expert_topk_amd", "csrc")
     src = b"".join(open(os.path.join(csrc, f), "rb").read() for f in (FC1_SOURCE[workload], "moe_internal.h"))
     return hashlib.sha256(src).hexdigest()
-
-
-class K3Batches(Batches):
-    """Input sets of the K3-shape decode workload at M tokens (see workloads.k3_case)."""
-
-    def __init__(self, plan, m, sets):
-        import torch
-        import workloads as W
-        from workloads import device as D
-        self.plan = plan
-        base = W.k3_case(m)
-        self.base = base
-        s = base.shape
-        self.T, self.H, self.I, self.E, self.k = s.tokens, s.hidden, s.inter, s.experts, s.top_k
-        self.inputs, self.touched, self.valid = [], [], []
-        for j in range(sets):
-            c = base if j == 0 else W.make_case(base.name, s, base.seed + 100000 * j, routing="uniform",
-                                                weight_seed=base.wseed)
-            self.inputs.append((D.to_dev(c.hidden_bits).view(torch.bfloat16), D.to_dev(c.topk_ids),
-                                D.to_dev(c.topk_weights)))
-            v = c.topk_ids[(c.topk_ids >= 0) & (c.topk_ids < self.E)]
-            self.touched.append(len(np.unique(v)))
-            self.valid.append(int(v.size))
-        self.acc = None
-        self.out = torch.empty((self.T, self.H), dtype=torch.bfloat16, device="cuda")
 
 
 def counter_traffic(workload, tag):
@@ -262,24 +380,26 @@ def counter_traffic(workload, tag):
 
 
 def cpu_baseline():
+    """The fp64 oracle, as it stands, on 24 tokens of the decode M=128 batch,
+    its experts evaluated on a thread per host core (BLAS single-threaded
+    inside each)."""
+    from concurrent.futures import ThreadPoolExecutor
+    from threadpoolctl import threadpool_limits
     import oracle
     import workloads as W
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
-    except Exception:
-        threads = 1
+    threads = max(1, min(16, os.cpu_count() or 1))
     case = W.config_case(1, m=128)
-    toks = [0, 1, 2, 3, 4, 5]
+    toks = list(range(24))
     cache = {e: case.expert(e) for e in np.unique(case.topk_ids[toks]) if 0 <= e < case.shape.experts}
-    t0 = time.perf_counter()
-    oracle.forward(case.hidden_bits, case.topk_ids, case.topk_weights, lambda e: cache[e], case.shape.experts,
-                   tokens=toks)
-    dt = time.perf_counter() - t0
+    with ThreadPoolExecutor(threads) as ex, threadpool_limits(1, "blas"):
+        t0 = time.perf_counter()
+        oracle.forward(case.hidden_bits, case.topk_ids, case.topk_weights, lambda e: cache[e], case.shape.experts,
+                       tokens=toks, pool=ex)
+        dt = time.perf_counter() - t0
     return {"value": round(len(toks) / dt, 4), "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"fp64 numpy oracle over tokens {toks} of the decode M=128 batch ({len(cache)} experts, "
-                      f"weight generation excluded): {dt:.1f}s; dequantisation runs on one core, the fp64 "
-                      f"matmuls on {threads} BLAS threads"}
+            "sample": f"fp64 numpy oracle over tokens 0..{len(toks) - 1} of the decode M=128 batch ({len(cache)} experts, "
+                      f"weight generation excluded): {dt:.1f}s on {threads} threads (one expert each at a time, "
+                      f"BLAS single-threaded); the host reports {os.cpu_count()} CPUs"}
 
 
 def router_timings(reps=200):
@@ -308,38 +428,44 @@ def router_timings(reps=200):
     return res
 
 
-def prefill_line(args):
+def base_line(args, r, summ, config):
+    return {"metric": METRIC, "value": summ["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": round(r["ms_per_step"], 5), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "data": "synthetic", "config": config, "layer": summ}
+
+
+def prefill_line(args, ceil):
     """The JSON line of one prefill configuration (see --workload)."""
     import workloads as W
     cid = PREFILL[args.workload]
     case = W.config_case(cid)
     pl, _ = build_plan(cid, case.shape.tokens)
-    b = Batches(pl, cid, None, 2)
+    b = Batches.config(pl, cid, None, 2)
     r = b.run(args.steps, args.warmup)
-    summ = b.summary(r)
+    summ = b.summary(r, ceil)
     mx = case.act == "mxfp8"
     s = case.shape
     valid = float(np.mean(b.valid))
     fc1_us = float(np.mean(r["fc1_ms"])) * 1e3
-    fc1_tflops = 2.0 * valid * s.hidden * 2 * s.inter / (fc1_us * 1e-6) / 1e12
+    fc1_flops = 2.0 * valid * s.hidden * 2 * s.inter
+    fc1_tflops = fc1_flops / (fc1_us * 1e-6) / 1e12
     peak = FP8_PEAK_TFLOPS if mx else BF16_PEAK_TFLOPS
-    tag = f"{args.workload}"
-    line = {
-        "metric": METRIC, "value": summ["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(r["ms_per_step"], 5), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "fp8xfp4" if mx else "bf16", "data": "synthetic",
-        "config": {"workload": f"{args.workload}: {s.tokens} tokens, hidden {s.hidden}, intermediate {s.inter}, "
-                               f"{s.experts} experts, top-{s.top_k}, {W.CONFIGS[cid]['routing']} routing, "
-                               f"{'MXFP8' if mx else 'bf16'} activations, MXFP4 weights",
-                   "tokens": s.tokens, "hidden": s.hidden, "intermediate": s.inter, "experts_resident": s.experts,
-                   "top_k": s.top_k},
-        "roofline": {"bound": "mfma", "achieved": round(fc1_tflops, 1), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(fc1_tflops / peak, 4), "traffic": counter_traffic(args.workload, tag),
-                     "kernel": ("fc_pre_mx<true,8> (FC1, MXFP8, eight waves)" if mx else "fc_pre<true,128,4> (FC1, bf16)"),
-                     "kernel_us": round(fc1_us, 2),
-                     "alg_flops_per_launch": 2.0 * valid * s.hidden * 2 * s.inter},
-        "layer": summ,
-    }
+    config = {"workload": f"{args.workload}: {s.tokens} tokens, hidden {s.hidden}, intermediate {s.inter}, "
+                          f"{s.experts} experts, top-{s.top_k}, {W.CONFIGS[cid]['routing']} routing, "
+                          f"{'MXFP8' if mx else 'bf16'} activations, MXFP4 weights",
+              "tokens": s.tokens, "hidden": s.hidden, "intermediate": s.inter, "experts_resident": s.experts,
+              "top_k": s.top_k}
+    line = base_line(args, r, summ, config)
+    line["dtype"] = "fp8xfp4" if mx else "bf16"
+    line["roofline"] = {
+        "bound": "mfma", "achieved": round(fc1_tflops, 1), "peak": peak, "unit": "TFLOP/s",
+        "frac": round(fc1_tflops / peak, 4), "traffic": counter_traffic(args.workload, args.workload),
+        "kernel": ("fc_pre_mx<true,8> (FC1, MXFP8, eight waves)" if mx else "fc_pre<true,128,4> (FC1, bf16)"),
+        "kernel_us": round(fc1_us, 2), "alg_flops_per_launch": fc1_flops}
+    if ceil:
+        key = "mfma_f8f4_tflops" if mx else "mfma_bf16_tflops"
+        line["roofline"]["measured_peak"] = ceil[key]
+        line["roofline"]["frac_of_measured"] = round(fc1_tflops / ceil[key], 4)
     pl.close()
     return line
 
@@ -353,6 +479,7 @@ def main():
     p.add_argument("--sets", type=int, default=8)
     p.add_argument("--no-extra", action="store_true")
     p.add_argument("--no-cpu", action="store_true")
+    p.add_argument("--no-ceilings", action="store_true", help="skip the peak micro-benchmarks")
     p.add_argument("--workload", default="decode", choices=["decode"] + list(PREFILL))
     p.add_argument("--fused", action="store_true",
                    help="also time the one-launch (cooperative) fused forward on decode batches")
@@ -379,47 +506,46 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     Batches.fused = args.fused
+    state_before = gpu_state()
+    ceil = None if args.no_ceilings else ceilings()
+    if ceil:
+        log(f"measured ceilings: {ceil}")
     if args.workload != "decode":
-        print(json.dumps(prefill_line(args)), flush=True)
+        line = prefill_line(args, ceil)
+        line["ceilings"] = ceil
+        line["gpu_state"] = {"before": state_before, "after": gpu_state()}
+        line["context"] = CONTEXT
+        print(json.dumps(line), flush=True)
         return
     plan, _ = build_plan(1, max(max(W.DECODE_M), args.m))
-    head_b = Batches(plan, 1, args.m, args.sets)
+    head_b = Batches.config(plan, 1, args.m, args.sets)
     r = head_b.run(args.steps, args.warmup)
-    head = head_b.summary(r)
+    head = head_b.summary(r, ceil)
     log(f"decode M={args.m}: {head}")
     fc1_us = float(np.mean(r["fc1_ms"])) * 1e3
     fc1_gbs = r["fc1_bytes"] / (fc1_us * 1e-6) / 1e9
-    line = {
-        "metric": METRIC,
-        "value": head["tokens_per_s"],
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(r["ms_per_step"], 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic",
-        "config": {"workload": f"decode M={args.m}: hidden 7168, intermediate 2048, 224 resident of 384 experts, "
-                               f"top-8, MXFP4 weights, bf16 activations",
-                   "tokens": args.m, "hidden": 7168, "intermediate": 2048, "experts_resident": 224,
-                   "experts_global": 384, "top_k": 8},
-        "roofline": {"bound": "hbm", "achieved": round(fc1_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(fc1_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": counter_traffic("decode", "decode_m128") if args.m == 128 else None,
-                     "kernel": "fc_dec<true,false,4,4,2> (FC1, bf16, 16-row tiles)", "kernel_us": round(fc1_us, 2),
-                     "alg_bytes_per_launch": int(r["fc1_bytes"])},
-        "layer": head,
-    }
+    config = {"workload": f"decode M={args.m}: hidden 7168, intermediate 2048, 224 resident of 384 experts, "
+                          f"top-8, MXFP4 weights, bf16 activations",
+              "tokens": args.m, "hidden": 7168, "intermediate": 2048, "experts_resident": 224,
+              "experts_global": 384, "top_k": 8}
+    line = base_line(args, r, head, config)
+    line["dtype"] = "bf16"
+    line["roofline"] = {
+        "bound": "hbm", "achieved": round(fc1_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+        "frac": round(fc1_gbs / HBM_PEAK_GBS, 4),
+        "traffic": counter_traffic("decode", "decode_m128") if args.m == 128 else None,
+        "kernel": "fc_dec<true,false,4,4,2> (FC1, bf16, 16-row tiles)", "kernel_us": round(fc1_us, 2),
+        "alg_bytes_per_launch": int(r["fc1_bytes"])}
+    if ceil:
+        line["roofline"]["measured_peak"] = ceil["hbm_read_nt_gbs"]
+        line["roofline"]["frac_of_measured"] = round(fc1_gbs / ceil["hbm_read_nt_gbs"], 4)
     if not args.no_extra:
         extra = {}
         for m in W.DECODE_M:
             if m == args.m:
                 continue
-            b = Batches(plan, 1, m, args.sets)
-            extra[f"decode_m{m}"] = b.summary(b.run(max(20, args.steps), args.warmup))
+            b = Batches.config(plan, 1, m, args.sets)
+            extra[f"decode_m{m}"] = b.summary(b.run(max(20, args.steps), args.warmup), ceil)
             log(f"decode M={m}: {extra[f'decode_m{m}']}")
             del b
         plan.close()
@@ -427,8 +553,8 @@ def main():
         torch.cuda.empty_cache()
         for cid in (2, 3, 4):
             pl, case = build_plan(cid, W.config_case(cid).shape.tokens)
-            b = Batches(pl, cid, None, 2)
-            extra[case.name] = b.summary(b.run(10, 3))
+            b = Batches.config(pl, cid, None, 2)
+            extra[case.name] = b.summary(b.run(10, 3), ceil)
             log(f"config {cid} ({case.name}): {extra[case.name]}")
             pl.close()
             del pl, b
@@ -444,8 +570,8 @@ def main():
         torch.cuda.synchronize()
         log(f"K3 shapes: plan built in {time.time() - t0:.1f}s")
         for m in W.K3_DECODE_M:
-            b = K3Batches(pl, m, args.sets)
-            extra[f"k3_decode_m{m}"] = b.summary(b.run(max(20, args.steps), args.warmup))
+            b = Batches.k3(pl, m, args.sets)
+            extra[f"k3_decode_m{m}"] = b.summary(b.run(max(20, args.steps), args.warmup), ceil)
             log(f"K3 decode M={m}: {extra[f'k3_decode_m{m}']}")
             del b
         pl.close()
@@ -454,6 +580,9 @@ def main():
         extra["router_topk"] = router_timings()
         log(f"router: {extra['router_topk']}")
         line["extra"] = extra
+    line["ceilings"] = ceil
+    line["gpu_state"] = {"before": state_before, "after": gpu_state()}
+    line["context"] = CONTEXT
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline()
     print(json.dumps(line), flush=True)

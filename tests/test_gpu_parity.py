@@ -5,10 +5,12 @@ or 4e-3 relative L2 of the oracle (oracle.check_rows), and out_bf16 equal
 bit for bit to RNE_bf16(acc_fp32).  Every token of every case is compared,
 the full-size configurations included (the oracle evaluates the experts on a
 thread pool).  MXFP8 path: the device's requantised h (E4M3 codes and E8M0
-bytes, read back from the workspace) must equal the oracle's MXFP8 of the
-exact h except where the oracle proves the decision ambiguous (the exact h
-within fp32 evaluation error of a rounding or scale decision); the layer is
-then checked by the plain rule against the oracle evaluated from that h.
+bytes, read back from the workspace) is compared code by code with the
+oracle's MXFP8 of the exact h -- at most 0.1 % may differ, each by one E4M3
+step from the exact h or by less than 2^-12 of its block's largest |h| -- and
+the counts are reported (how many decisions an fp32 evaluation could flip, how
+many differ, how many beyond fp32 rounding); the oracle then continues from
+those codes, and the layer meets the same plain rule (no slack).
 """
 import os
 import sys
@@ -74,22 +76,31 @@ def reference(case, tokens=None, ew=None, h_requant=None):
                               tokens=tokens, h_requant=h_requant, pool=oracle_pool())
 
 
+H_DEVIATION_BOUND = 2.0 ** -12     # of the largest |h| of the element's 32-element block
+
+
 def device_h_requant(case, plan, stats, workspace=None):
     """oracle.forward's h_requant hook: the device's MXFP8 h of each route (row
     rowpos[t*k+s] of the workspace regions, rowpos from the oracle's route
-    sort), checked element by element, the counts going to `stats`:
-      n_ambiguous  codes the oracle cannot fix from an fp32 evaluation of h
-                   (oracle.h_uncertainty: the exact h lies within an fp32
-                   dot product's rounding of a rounding or scale decision);
-      n_differ     device codes other than the oracle's MXFP8 of the exact h;
-      n_beyond_fp32  of those, codes outside the fp32 band: the scaled MFMA sums
-                   a 128-product block with fewer bits than fp32 (measured by
-                   test_scaled_mfma_block_summation), so h lands on the other
-                   side of a decision a little more often;
-      n_bad        codes more than one E4M3 step from the exact h (at the
-                   device's block scale) -- none is allowed.
-    The layer is then evaluated from the device's codes, which equal the
-    oracle's everywhere else."""
+    sort) compared code by code with the oracle's MXFP8 of the exact h.  The
+    oracle continues from the device's codes: they equal its own except at
+    the few positions counted here, each checked by the caller to be one E4M3
+    step from the exact h or within 2^-12 of its block's largest |h|.  (A
+    single such step on a large element moves a row by about 2^-4 / sqrt(I);
+    at I = 384 that alone can exceed the 4e-3 bound.)  Counts go to `stats`:
+      n_ambiguous    codes an fp32 evaluation of h could legitimately flip
+                     (oracle.h_uncertainty: the exact h lies within an fp32 dot
+                     product's rounding of a rounding or scale decision);
+      n_differ       device codes other than the oracle's;
+      n_beyond_fp32  of those, codes outside that fp32 band, and
+      n_beyond_step  codes more than one E4M3 step from the exact h: the scaled
+                     MFMA sums a 128-product block with fewer bits than fp32
+                     (test_scaled_mfma_block_summation), so small elements of a
+                     block with a large maximum can move by several of their
+                     (subnormal) steps;
+      max_dev        of the codes more than one step off, the largest distance
+                     between the device code's value and the oracle's, over the
+                     largest |h| of its block."""
     s = case.shape
     rows_all = plan.cfg.max_tokens * s.top_k
     hq = plan.workspace_region(moe.MOE_WS_H_CODES, workspace).view(rows_all, s.inter).cpu().numpy()
@@ -102,18 +113,27 @@ def device_h_requant(case, plan, stats, workspace=None):
         codes, scales = hq[rows], hs[rows]
         band = oracle.mxfp8_requant_check(h, dh, codes, scales)
         step = oracle.mxfp8_requant_check(h, oracle.mxfp8_quantum(h), codes, scales)
+        amax = np.repeat(np.abs(h.reshape(len(rows), -1, 32)).max(axis=2), 32, axis=1)
+        with np.errstate(invalid="ignore", divide="ignore"):
+            dev = np.where(amax > 0, np.abs(step["values"] - band["rt"]) / np.where(amax > 0, amax, 1.0), 0.0)
         with lock:
             stats["n"] += band["n"]
             stats["n_ambiguous"] += band["n_ambiguous"]
             stats["n_differ"] += int((step["values"] != band["rt"]).sum())
             stats["n_beyond_fp32"] += band["n_bad"]
-            stats["n_bad"] += step["n_bad"]
-            for i, c in np.argwhere(~step["admissible"])[:4]:
-                say(f"  wrong h code: expert {e} route {routes[i]} column {c}: exact h {h[i, c]!r}, "
-                    f"oracle {band['rt'][i, c]!r}, device {step['values'][i, c]!r}, device scale byte "
-                    f"{int(scales[i, c // 32])}")
+            stats["n_beyond_step"] += step["n_bad"]
+            far = ~step["admissible"]                     # more than one step from the exact h
+            if far.any():
+                stats["max_dev"] = max(stats["max_dev"], float(np.nan_to_num(dev[far], nan=np.inf).max()))
+            for i, c in np.argwhere(far & ~(dev <= H_DEVIATION_BOUND))[:4]:
+                say(f"  h code beyond the bound: expert {e} route {routes[i]} column {c}: exact h {h[i, c]!r}, "
+                    f"oracle {band['rt'][i, c]!r}, device {step['values'][i, c]!r}, block max {amax[i, c]!r}")
         return step["values"]
     return take
+
+
+def new_h_stats():
+    return dict(n=0, n_ambiguous=0, n_differ=0, n_beyond_fp32=0, n_beyond_step=0, max_dev=0.0)
 
 
 def check_layer(case, out, acc, tokens=None, ew=None, plan=None, workspace=None):
@@ -124,15 +144,16 @@ def check_layer(case, out, acc, tokens=None, ew=None, plan=None, workspace=None)
     hook = None
     if case.act == "mxfp8":
         assert plan is not None, "the MXFP8 check reads the forward's h from the plan's workspace"
-        stats = dict(n=0, n_ambiguous=0, n_differ=0, n_beyond_fp32=0, n_bad=0)
+        stats = new_h_stats()
         hook = device_h_requant(case, plan, stats, workspace)
     ref = reference(case, sel, ew, hook)
     if stats is not None:
-        say(f"  h codes: {stats['n']} checked, {stats['n_ambiguous']} ambiguous under fp32 rounding, "
-            f"{stats['n_differ']} differ from the oracle's ({stats['n_beyond_fp32']} beyond fp32 rounding), "
-            f"{stats['n_bad']} more than one step off")
-        assert stats["n_bad"] == 0, f"{case.name}: {stats['n_bad']} requantised h codes are off by more than a step"
+        say(f"  h codes: {stats['n']} checked, {stats['n_ambiguous']} ambiguous under fp32 rounding; "
+            f"{stats['n_differ']} differ from the oracle's ({stats['n_beyond_fp32']} beyond fp32 rounding, "
+            f"{stats['n_beyond_step']} by more than one step, at most {stats['max_dev']:.2e} of the block "
+            f"maximum)")
         assert stats["n_differ"] <= 1e-3 * stats["n"], f"{case.name}: {stats}"
+        assert stats["max_dev"] <= H_DEVIATION_BOUND, f"{case.name}: {stats}"
     out_bits = G.bf16_bits(out)[sel]
     out_v = oracle.bf16_bits_to_f64(out_bits)
     r_out = oracle.check_rows(out_v, ref)
@@ -620,15 +641,16 @@ def test_negative_control_swapped_nibbles_fail_the_check(act, T):
     plan, _ = G.make_plan(case, weights=[_swap_nibbles(w[0]), w[1], _swap_nibbles(w[2]), w[3]])
     out, acc = G.run_forward(plan, case)
     assert torch.isfinite(acc).all()
-    stats = dict(n=0, n_ambiguous=0, n_differ=0, n_beyond_fp32=0, n_bad=0)
+    stats = new_h_stats()
     hook = device_h_requant(case, plan, stats) if act == "mxfp8" else None
     ref = reference(case, h_requant=hook)
     rl2 = [oracle.rel_l2(a, b) for a, b in zip(acc.cpu().numpy(), ref) if np.linalg.norm(b) > 0]
-    say(f"  rel_l2 min {min(rl2):.2f} median {np.median(rl2):.2f}; h codes wrong: {stats['n_bad']} of {stats['n']}")
+    say(f"  rel_l2 min {min(rl2):.2f} median {np.median(rl2):.2f}; h codes differing: {stats['n_differ']} of "
+        f"{stats['n']}")
     assert min(rl2) > 0.5
     assert not oracle.check_rows(acc.cpu().numpy(), ref)["pass"]
     if act == "mxfp8":
-        assert stats["n_bad"] > 0.5 * stats["n"]
+        assert stats["n_differ"] > 0.5 * stats["n"] and stats["max_dev"] > H_DEVIATION_BOUND
     # the same plan over the true weights passes
     plan2, _ = G.make_plan(case, weights=w)
     out2, acc2 = G.run_forward(plan2, case)
@@ -787,8 +809,10 @@ def test_scaled_mfma_block_summation():
     every product (and C) lies in one binade the result is the exact sum;
     across a wide range of magnitudes it is not an fp32-rounded sum -- the
     small products lose their low bits against the largest -- but the error
-    stays under 2^-10 of the largest term.  This is why the MXFP8 check allows
-    h codes one E4M3 step off beyond fp32 rounding."""
+    stays under 2^-10 of the largest term.  This is why an MXFP8 h code can
+    differ from the oracle's beyond fp32 rounding (small elements of a block
+    with a large maximum by a few of their steps), which the layer check
+    against the pure oracle absorbs."""
     rng = np.random.default_rng(17)
     for one_binade, c_scale in ((True, 0.0), (False, 0.0), (False, 64.0)):
         lanes, exact, maxterm = _mfma_blocks(rng, 512, one_binade, c_scale)
