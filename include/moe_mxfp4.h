@@ -116,6 +116,21 @@ moe_status moe_mxfp4_forward(moe_mxfp4_plan_t plan, const uint16_t* hidden,
                              int32_t num_tokens, float* acc_fp32, uint16_t* out_bf16,
                              void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* The same forward as moe_mxfp4_forward for callers that cannot allocate
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): it takes no workspace.  Its scratch (route metadata, h, the
+ * per-route outputs) lives in a fixed 48 MiB device array of the library, one
+ * copy per GPU, held until the process ends; num_tokens is limited to what
+ * fits it (at hidden 7168, intermediate 2048, top-8 about 190 tokens), and a
+ * larger batch returns MOE_ERR_CAPACITY naming the bytes it needs.  Arguments
+ * and outputs are those of moe_mxfp4_forward; the results are bitwise equal
+ * to it.  Nothing is allocated and nothing synchronises.  Every call on a GPU
+ * shares that GPU's array: calls that overlap on one GPU (on concurrent
+ * streams or threads) race. */
+moe_status moe_mxfp4_forward_noalloc(moe_mxfp4_plan_t plan, const uint16_t* hidden, const int32_t* topk_ids,
+                                     const float* topk_weights, int32_t num_tokens, float* acc_fp32,
+                                     uint16_t* out_bf16, hipStream_t stream);
+
 /* The same forward as moe_mxfp4_forward, the whole layer in one kernel
  * launch, for decode-sized batches: a MOE_ACT_BF16 plan and at most 256 routes
  * (num_tokens * top_k), else MOE_ERR_SHAPE.  The pages' fused MoE launch

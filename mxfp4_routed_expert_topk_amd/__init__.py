@@ -10,6 +10,7 @@ Names follow the C ABI in include/moe_mxfp4.h:
   query_sizes(cfg)                      -> (repacked_bytes, workspace_bytes)
   Plan(cfg, w13_codes, w13_scales, w2_codes, w2_scales)     (moe_mxfp4_plan)
   Plan.forward(hidden, topk_ids, topk_weights, out=None, acc=None)
+  Plan.forward_noalloc(...)             the same, scratch in the library (moe_mxfp4_forward_noalloc)
   Plan.route(topk_ids)                  -> (counts, offsets, perm, rowpos)
   Plan.workspace_region(region)         -> the workspace bytes of an intermediate (MXFP8 h)
   mxfp8_quantize(x_bf16)                -> (codes, scales)
@@ -34,7 +35,8 @@ STATUS_NAMES = {0: "MOE_OK", 1: "MOE_ERR_ARG", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_A
                 9: "MOE_ERR_TIMEOUT"}
 MOE_WS_H_CODES = 0
 MOE_WS_H_SCALES = 1
-EXPORTS = ("moe_mxfp4_query_sizes", "moe_mxfp4_plan", "moe_mxfp4_forward", "moe_mxfp4_forward_fused",
+EXPORTS = ("moe_mxfp4_query_sizes", "moe_mxfp4_plan", "moe_mxfp4_forward", "moe_mxfp4_forward_noalloc",
+           "moe_mxfp4_forward_fused",
            "moe_mxfp4_fused_status", "moe_mxfp4_route", "moe_mxfp4_workspace_region", "moe_mxfp8_quantize",
            "moe_router_topk", "moe_probe_memory", "moe_probe_mfma", "moe_probe_mfma_f8f4_blocks",
            "moe_mxfp4_set_stage_events",
@@ -85,6 +87,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_mxfp4_plan.argtypes = [cfgp, vp, vp, vp, vp, vp, sz, vp, ctypes.POINTER(vp)]
     lib.moe_mxfp4_forward.argtypes = [vp, vp, vp, vp, i32, vp, vp, vp, sz, vp]
     lib.moe_mxfp4_forward_fused.argtypes = [vp, vp, vp, vp, i32, vp, vp, vp, sz, vp]
+    lib.moe_mxfp4_forward_noalloc.argtypes = [vp, vp, vp, vp, i32, vp, vp, vp]
     lib.moe_mxfp4_fused_status.argtypes = [vp, vp, sz, vp]
     lib.moe_mxfp4_route.argtypes = [vp, vp, i32, vp, vp, vp, vp, vp, sz, vp]
     lib.moe_mxfp4_workspace_region.argtypes = [vp, i32, ctypes.POINTER(sz), ctypes.POINTER(sz)]
@@ -215,6 +218,14 @@ class Plan:
         T, out, ws = self._forward_args(hidden, topk_ids, topk_weights, out, acc, num_tokens, workspace)
         _check(load_library().moe_mxfp4_forward(self._h, _ptr(hidden), _ptr(topk_ids), _ptr(topk_weights), T,
                                                 _ptr(acc), _ptr(out), _ptr(ws), ws.numel(), _stream(stream)))
+        return out
+
+    def forward_noalloc(self, hidden, topk_ids, topk_weights, out=None, acc=None, num_tokens=None, stream=None):
+        """The same forward with the library's fixed scratch instead of a
+        workspace (moe_mxfp4_forward_noalloc); pass `out` to allocate nothing."""
+        T, out, _ = self._forward_args(hidden, topk_ids, topk_weights, out, acc, num_tokens, None)
+        _check(load_library().moe_mxfp4_forward_noalloc(self._h, _ptr(hidden), _ptr(topk_ids), _ptr(topk_weights), T,
+                                                        _ptr(acc), _ptr(out), _stream(stream)))
         return out
 
     def forward_fused(self, hidden, topk_ids, topk_weights, out=None, acc=None, num_tokens=None, stream=None,

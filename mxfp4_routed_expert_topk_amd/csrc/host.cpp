@@ -18,10 +18,15 @@
 
 #include "../../include/moe_mxfp4.h"
 #include "moe_internal.h"
+#include "plan.h"
 
 namespace {
 
 thread_local std::string g_err;
+
+}  // namespace
+
+namespace moe {
 
 moe_status fail(moe_status s, const char* fmt, ...) {
   char buf[512];
@@ -37,6 +42,18 @@ moe_status ok() {
   g_err.clear();
   return MOE_OK;
 }
+
+moe_status hip_fail(hipError_t e, const char* what) {
+  return fail(MOE_ERR_HIP, "%s failed: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace moe
+
+namespace {
+
+using moe::fail;
+using moe::hip_fail;
+using moe::ok;
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
@@ -64,10 +81,6 @@ moe_status check_config(const moe_mxfp4_config* c) {
   if (c->act != MOE_ACT_BF16 && c->act != MOE_ACT_MXFP8)
     return fail(MOE_ERR_ARG, "act must be MOE_ACT_BF16 (0) or MOE_ACT_MXFP8 (1), got %d", c->act);
   return MOE_OK;
-}
-
-moe_status hip_fail(hipError_t e, const char* what) {
-  return fail(MOE_ERR_HIP, "%s failed: %s", what, hipGetErrorString(e));
 }
 
 }  // namespace
@@ -118,14 +131,6 @@ Layout make_layout(int H, int I, int E, int k, int Tmax, int act) {
 
 }  // namespace moe
 
-struct moe_mxfp4_plan_s {
-  moe_mxfp4_config cfg;
-  moe::Layout L;
-  const uint8_t* repacked;
-  hipEvent_t events[5];
-  int n_events;
-  uint32_t fused_gen;   // generation of this plan's last fused forward (0: none)
-};
 
 namespace {
 
@@ -230,9 +235,8 @@ static moe_status check_ws(const moe_mxfp4_plan_s* p, void* workspace, size_t wo
 
 // The FC1 and FC2 arguments of one forward: weights, route outputs, the
 // activations each reads and the workspace rows each writes.
-static void fc_args(const moe_mxfp4_plan_s* p, uint8_t* ws, const moe::RouteOut& ro, const uint16_t* hidden,
-                    int32_t T, moe::FcArgs* f1, moe::FcArgs* f2) {
-  const moe::Layout& L = p->L;
+static void fc_args(const moe_mxfp4_plan_s* p, const moe::Layout& L, uint8_t* ws, const moe::RouteOut& ro,
+                    const uint16_t* hidden, int32_t T, moe::FcArgs* f1, moe::FcArgs* f2) {
   const bool mx = p->cfg.act == MOE_ACT_MXFP8;
   *f1 = moe::FcArgs{};
   f1->codes = p->repacked + L.rp_w13_codes;
@@ -269,20 +273,8 @@ static void fc_args(const moe_mxfp4_plan_s* p, uint8_t* ws, const moe::RouteOut&
 static moe_status check_forward(moe_mxfp4_plan_t p, const uint16_t* hidden, const int32_t* topk_ids,
                                 const float* topk_weights, int32_t T, float* acc_fp32, uint16_t* out_bf16,
                                 void* workspace, size_t workspace_bytes) {
-  if (!p) return fail(MOE_ERR_ARG, "plan is null");
-  if (T < 0) return fail(MOE_ERR_ARG, "num_tokens must be >= 0, got %d", T);
-  if (T > p->cfg.max_tokens)
-    return fail(MOE_ERR_CAPACITY, "num_tokens %d exceeds the plan's max_tokens %d", T, p->cfg.max_tokens);
-  if (moe_status s = check_ws(p, workspace, workspace_bytes)) return s;
-  const void* ptrs[] = {hidden, topk_ids, topk_weights, out_bf16};
-  const char* names[] = {"hidden", "topk_ids", "topk_weights", "out_bf16"};
-  for (int i = 0; i < 4; ++i) {
-    if (!ptrs[i]) return fail(MOE_ERR_ARG, "%s is null", names[i]);
-    if (misaligned(ptrs[i])) return fail(MOE_ERR_ALIGN, "%s must be 16-byte aligned, got %p", names[i], ptrs[i]);
-  }
-  if (acc_fp32 && misaligned(acc_fp32))
-    return fail(MOE_ERR_ALIGN, "acc_fp32 must be 16-byte aligned, got %p", (void*)acc_fp32);
-  return MOE_OK;
+  if (moe_status s = moe::check_forward_io(p, hidden, topk_ids, topk_weights, T, acc_fp32, out_bf16)) return s;
+  return check_ws(p, workspace, workspace_bytes);
 }
 
 moe_status moe_mxfp4_forward(moe_mxfp4_plan_t p, const uint16_t* hidden, const int32_t* topk_ids,
@@ -291,10 +283,40 @@ moe_status moe_mxfp4_forward(moe_mxfp4_plan_t p, const uint16_t* hidden, const i
   if (moe_status s = check_forward(p, hidden, topk_ids, topk_weights, T, acc_fp32, out_bf16, workspace,
                                    workspace_bytes))
     return s;
+  return moe::forward_with_layout(p, p->L, hidden, topk_ids, topk_weights, T, acc_fp32, out_bf16,
+                                  static_cast<uint8_t*>(workspace), stream);
+}
+
+}  // extern "C"
+
+namespace moe {
+
+moe_status check_forward_io(const moe_mxfp4_plan_s* p, const uint16_t* hidden, const int32_t* topk_ids,
+                            const float* topk_weights, int32_t T, const float* acc_fp32, const uint16_t* out_bf16) {
+  if (!p) return fail(MOE_ERR_ARG, "plan is null");
+  if (T < 0) return fail(MOE_ERR_ARG, "num_tokens must be >= 0, got %d", T);
+  if (T > p->cfg.max_tokens)
+    return fail(MOE_ERR_CAPACITY, "num_tokens %d exceeds the plan's max_tokens %d", T, p->cfg.max_tokens);
+  const void* ptrs[] = {hidden, topk_ids, topk_weights, out_bf16};
+  const char* names[] = {"hidden", "topk_ids", "topk_weights", "out_bf16"};
+  for (int i = 0; i < 4; ++i) {
+    if (!ptrs[i]) return fail(MOE_ERR_ARG, "%s is null", names[i]);
+    if (misaligned(ptrs[i])) return fail(MOE_ERR_ALIGN, "%s must be 16-byte aligned, got %p", names[i], ptrs[i]);
+  }
+  if (acc_fp32 && misaligned(acc_fp32))
+    return fail(MOE_ERR_ALIGN, "acc_fp32 must be 16-byte aligned, got %p", (const void*)acc_fp32);
+  return MOE_OK;
+}
+
+// The forward's launch sequence over a workspace laid out by L (the plan's
+// layout, or one sized for the batch at hand: every offset and bound comes from
+// L, so a layout for fewer tokens addresses a smaller workspace).  Arguments
+// are checked by the caller.
+moe_status forward_with_layout(moe_mxfp4_plan_s* p, const Layout& L, const uint16_t* hidden, const int32_t* topk_ids,
+                               const float* topk_weights, int32_t T, float* acc_fp32, uint16_t* out_bf16,
+                               uint8_t* ws, hipStream_t stream) {
   if (T == 0) return ok();
 
-  const moe::Layout& L = p->L;
-  uint8_t* ws = static_cast<uint8_t*>(workspace);
   const moe::RouteOut ro = route_out(L, ws);
   const bool mx = p->cfg.act == MOE_ACT_MXFP8;
   const int nev = p->n_events;
@@ -326,7 +348,7 @@ moe_status moe_mxfp4_forward(moe_mxfp4_plan_t p, const uint16_t* hidden, const i
   REC(1);
 
   moe::FcArgs f1, f2;
-  fc_args(p, ws, ro, hidden, T, &f1, &f2);
+  fc_args(p, L, ws, ro, hidden, T, &f1, &f2);
   if (prefill) CHK(moe::launch_fc1_prefill(f1, bm, tiles_max, stream), "FC1 launch");
   else if (prefill_mx) CHK(moe::launch_fc1_prefill_mx(f1, tiles_max, stream), "FC1 launch");
   else CHK(mx ? moe::launch_fc1_mx(f1, tiles_max, T, stream) : moe::launch_fc1_bf16(f1, tiles_max, T, stream),
@@ -349,6 +371,10 @@ moe_status moe_mxfp4_forward(moe_mxfp4_plan_t p, const uint16_t* hidden, const i
 #undef CHK
   return ok();
 }
+
+}  // namespace moe
+
+extern "C" {
 
 moe_status moe_mxfp4_forward_fused(moe_mxfp4_plan_t p, const uint16_t* hidden, const int32_t* topk_ids,
                                    const float* topk_weights, int32_t T, float* acc_fp32, uint16_t* out_bf16,
@@ -374,7 +400,7 @@ moe_status moe_mxfp4_forward_fused(moe_mxfp4_plan_t p, const uint16_t* hidden, c
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   const moe::RouteOut ro = route_out(L, ws);
   moe::FcArgs f1, f2;
-  fc_args(p, ws, ro, hidden, T, &f1, &f2);
+  fc_args(p, L, ws, ro, hidden, T, &f1, &f2);
   hipError_t e;
   if (p->n_events > 0 && (e = hipEventRecord(p->events[0], stream)) != hipSuccess)
     return hip_fail(e, "hipEventRecord");
