@@ -20,8 +20,8 @@ peak of its dtype (extras and the CPU baseline are skipped).
 Prints ONE JSON line:
  * `value`: whole-job tokens/s of K back-to-back eager steps (one event pair);
  * `layer`: per-step event pairs -- median and p90 with warm caches, and again
-   with a 1 GiB write between steps (cold: nothing of the last step is left in
-   the caches) -- the same steps replayed from captured hipGraphs, per-stage
+   with 1 GiB of other data read between steps (cold: nothing of the last step
+   is left in the caches) -- the same steps replayed from captured hipGraphs, per-stage
    times, and a SHA-256 prefix of the output (input set 0);
  * `roofline`: the dominant kernel (FC1) timed by HIP events recorded on its
    launch stream, priced against the published peak and against the ceiling
@@ -212,14 +212,21 @@ class Batches:
         self.plan.forward(x, ids, wts, out=self.out, acc=self.acc)
 
     def _flush(self):
+        """Read 1 GiB of other data (the library's read probe): the caches then
+        hold none of the last step's weights, and nothing dirty is left to
+        write back during the next step (a write flush would leave that)."""
         import torch
+        import mxfp4_routed_expert_topk_amd as moe
         if self.flush_buf is None:
-            self.flush_buf = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
-        self.flush_buf.fill_(1)
+            self.flush_buf = torch.ones(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+            self.flush_sink = torch.empty(16384, dtype=torch.float32, device="cuda")
+            self.flush_grid = torch.cuda.get_device_properties(0).multi_processor_count * 8
+            torch.cuda.synchronize()
+        moe.probe_memory(moe.MOE_PROBE_READ, self.flush_buf, None, self.flush_sink, self.flush_grid)
 
     def per_step_times(self, steps, first, flush):
-        """One event pair per step; with `flush`, 1 GiB is written between steps
-        (outside the timed pairs)."""
+        """One event pair per step; with `flush`, 1 GiB of other data is read
+        between steps (outside the timed pairs)."""
         import torch
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
         torch.cuda.synchronize()
