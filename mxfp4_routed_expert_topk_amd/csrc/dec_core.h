@@ -1,0 +1,132 @@
+// The K loop of one wave of the 16-row decode FC kernels, shared by every
+// kernel that runs it (the grouped decode kernels, the small-batch kernels
+// and the single-launch fused forward), so a row's fp32 sum is formed by one
+// piece of code wherever it runs.
+//
+// A wave multiplies one 16-row A tile (row `arow` per lane: lane l holds row
+// l%16 of the tile, K group l/16) by NBW consecutive 16-row weight blocks
+// starting at block nb0 of expert e, over the 128-K column blocks [lo, hi) in
+// ascending order, streaming the repacked 1 KB tiles with 128-bit loads kept
+// P column blocks ahead of the MFMAs.
+//
+// bf16 path: A = bf16 activations, B = E2M1 codes dequantised in registers to
+// bf16 by the gfx950 scaled converter (value * 2^(scale-127), exact), four
+// v_mfma_f32_16x16x32_bf16 per column block.  MXFP8 path: A = E4M3 codes +
+// E8M0 per 32, B = the same E2M1 tiles + E8M0, one
+// v_mfma_scale_f32_16x16x128_f8f6f4 per column block, which applies both
+// block scales inside the instruction.
+#pragma once
+
+#include "moe_internal.h"
+
+namespace moe {
+
+template <bool MX>
+struct AFrag;
+template <>
+struct AFrag<false> { uint4 v[4]; };                 // 32 bf16 = K 32*kq .. +32 of one 128-K block
+template <>
+struct AFrag<true> { uint4 lo, hi; uint32_t scale; };  // 32 E4M3 + E8M0 of group kq
+
+// FC1's weight loads carry the non-temporal hint (each weight byte is read
+// once); FC2's measured faster as plain loads.
+template <bool FC1, bool MX, int NBW, int P>
+__device__ __forceinline__ void dec_kloop(const FcArgs& a, int e, int nb0, long long arow, int lo, int hi,
+                                          f32x4_t (&acc)[NBW]) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int kq = lane >> 4;
+  const MatLayout M = a.mat;
+  const uint8_t* cbase = a.codes + ((size_t)e * M.nb + nb0) * M.kb * kTileBytes + lane * 16;
+  const size_t cstride = (size_t)M.kb * kTileBytes;
+  const uint8_t* sbase = a.scales + ((size_t)e * M.nb + nb0) * M.kb4 * kScaleGroupBytes + lane * 4;
+  const size_t sstride = (size_t)M.kb4 * kScaleGroupBytes;
+  const int n = hi - lo;
+
+#pragma unroll
+  for (int j = 0; j < NBW; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  uint4 Wr[P][NBW];
+  uint32_t Sr[P][NBW];
+  AFrag<MX> Ar[P];
+
+  auto load = [&](uint4 (&w)[NBW], uint32_t (&s)[NBW], AFrag<MX>& af, int kb) {
+    kb = min(kb, hi - 1);
+#pragma unroll
+    for (int j = 0; j < NBW; ++j) {
+      const uint4* wp = reinterpret_cast<const uint4*>(cbase + j * cstride + (size_t)kb * kTileBytes);
+      if constexpr (FC1) {
+        typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+        const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(wp));
+        w[j] = make_uint4(v[0], v[1], v[2], v[3]);
+      } else {
+        w[j] = *wp;
+      }
+      s[j] = *reinterpret_cast<const uint32_t*>(sbase + j * sstride + (size_t)(kb >> 2) * kScaleGroupBytes);
+    }
+    if constexpr (!MX) {
+      const uint4* ap = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.a) + arow * a.lda +
+                                                       (size_t)kb * kTileK + kq * 32);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) af.v[q] = ap[q];
+    } else {
+      const uint8_t* ap = static_cast<const uint8_t*>(a.a) + arow * a.lda + (size_t)kb * kTileK + kq * 16;
+      af.lo = *reinterpret_cast<const uint4*>(ap);
+      af.hi = *reinterpret_cast<const uint4*>(ap + 64);
+      af.scale = a.a_scales[arow * (a.lda / 32) + kb * 4 + kq];
+    }
+  };
+
+  auto compute = [&](const uint4 (&w)[NBW], const uint32_t (&s)[NBW], const AFrag<MX>& af, int kb) {
+    const int sh = (kb & 3) * 8;
+    if constexpr (!MX) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const bf16x8_t A = __builtin_bit_cast(bf16x8_t, af.v[q]);
+#pragma unroll
+        for (int j = 0; j < NBW; ++j) {
+          const uint32_t wd = q == 0 ? w[j].x : q == 1 ? w[j].y : q == 2 ? w[j].z : w[j].w;
+          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, dequant8(wd, e8m0_to_f32((s[j] >> sh) & 0xFFu)),
+                                                           acc[j], 0, 0, 0);
+        }
+      }
+    } else {
+      const i32x8_t A = {(int)af.lo.x, (int)af.lo.y, (int)af.lo.z, (int)af.lo.w,
+                         (int)af.hi.x, (int)af.hi.y, (int)af.hi.z, (int)af.hi.w};
+#pragma unroll
+      for (int j = 0; j < NBW; ++j) {
+        const i32x8_t B = {(int)w[j].x, (int)w[j].y, (int)w[j].z, (int)w[j].w, 0, 0, 0, 0};
+        acc[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B, acc[j], 0, 4, 0, (int)af.scale, 0,
+                                                                  (int)((s[j] >> sh) & 0xFFu));
+      }
+    }
+  };
+
+  if (n > 0) {
+#pragma unroll
+    for (int p = 0; p < P; ++p) load(Wr[p], Sr[p], Ar[p], lo + p);
+    for (int it = 0; it < n; it += P) {
+#pragma unroll
+      for (int p = 0; p < P; ++p) {
+        if (it + p < n) {
+          compute(Wr[p], Sr[p], Ar[p], lo + it + p);
+          load(Wr[p], Sr[p], Ar[p], lo + it + p + P);
+        }
+      }
+    }
+  }
+}
+
+// K range of wave w of KSPLIT: contiguous ranges of ceil(kb / KSPLIT) column blocks.
+template <int KSPLIT>
+__device__ __forceinline__ void dec_krange(int kb, int w, int* lo, int* hi) {
+  const int per = (kb + KSPLIT - 1) / KSPLIT;
+  *lo = min(kb, w * per);
+  *hi = min(kb, *lo + per);
+}
+
+// The K split of a matrix: four ranges for long K (>= kKsplit4Blocks column
+// blocks), two otherwise -- a function of K alone, so every batch size and
+// kernel sums a row in the same order.
+__host__ __device__ constexpr int dec_ksplit(int kb) { return kb >= kKsplit4Blocks ? 4 : 2; }
+
+}  // namespace moe

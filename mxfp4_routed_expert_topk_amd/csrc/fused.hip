@@ -18,8 +18,8 @@
 // the error word takes the forward's generation, which makes every later wait
 // of that forward give up at once; the kernel always runs to its end.
 //
-// FC1 and FC2 items run the stand-alone decode kernels' item body
-// (dec_item.h) with the same K split per matrix, so every output element is
+// FC1 and FC2 items run the stand-alone decode kernels' K loop (dec_core.h)
+// with the same K split per matrix, so every output element is
 // summed over the same K ranges in the same order: the result is bitwise the
 // multi-launch forward's wherever that runs the decode kernels (it takes the
 // 128-row prefill kernels from 16 routes per expert on).  The combine item is
@@ -37,11 +37,76 @@
 // made a compare-and-swap loop retry its way to milliseconds.
 #include <atomic>
 
-#include "dec_item.h"
+#include "dec_core.h"
 #include "route_wave.h"
 
 namespace moe {
 namespace {
+
+// One work item of the 16-row decode FC kernels (FC1 with the SiLU gate, or
+// FC2): tile td = (expert, first row), group of SUBS x NBW weight row blocks,
+// on SUBS x KSPLIT waves: wave w takes K range w % KSPLIT of row blocks
+// NBW (SUBS group + w / KSPLIT) ..; the KSPLIT partial sums of a row block are
+// added in range order.  Every output element sees the K loop (dec_core.h)
+// and the range order of the 16-row kernels, whatever SUBS is.  The item ends
+// with all of its stores issued (a caller running items back to back puts a
+// barrier between them: the next item writes the same partial-sum LDS).
+template <bool FC1, bool MX, int NBW, int KSPLIT, int SUBS, int P>
+__device__ __forceinline__ void dec_item(const FcArgs& a, int2 td, int group) {
+  static_assert(!FC1 || NBW % 2 == 0, "FC1 groups hold gate/up pairs");
+  const int e = td.x, row0 = td.y;
+  const int rows = min(kBM, a.offsets[e + 1] - row0);
+  const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
+  const int sub = wv / KSPLIT, wave = wv % KSPLIT;   // column sub-group, K range
+  const int m = lane & 15, kq = lane >> 4;
+  const int mr = min(m, rows - 1);
+  const long long arow = FC1 ? (long long)(a.perm[row0 + mr] / a.top_k) : (long long)(row0 + mr);
+  const int nb0 = (group * SUBS + sub) * NBW;
+  int lo, hi;
+  dec_krange<KSPLIT>(a.mat.kb, wave, &lo, &hi);
+  f32x4_t acc[NBW];
+  dec_kloop<FC1, MX, NBW, P>(a, e, nb0, arow, lo, hi, acc);
+
+  __shared__ float red[SUBS * KSPLIT][NBW][4][kWave];
+#pragma unroll
+  for (int j = 0; j < NBW; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) red[wv][j][i][lane] = acc[j][i];
+  __syncthreads();
+  float (*rs)[NBW][4][kWave] = red + sub * KSPLIT;   // this sub-group's KSPLIT partial sets
+
+  constexpr int NEPI = FC1 ? NBW / 2 : NBW;   // output column blocks of the group
+  for (int c = wave; c < NEPI; c += KSPLIT) {
+    float v0[4], v1[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int j0 = FC1 ? 2 * c : c;
+      float s0 = rs[0][j0][i][lane], s1 = FC1 ? rs[0][j0 + 1][i][lane] : 0.f;
+#pragma unroll
+      for (int w = 1; w < KSPLIT; ++w) {
+        s0 += rs[w][j0][i][lane];
+        if (FC1) s1 += rs[w][j0 + 1][i][lane];
+      }
+      v0[i] = s0;
+      v1[i] = s1;
+    }
+    // D layout: lane holds rows 4*kq + i, column m
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 4 * kq + i;
+      if (r >= rows) continue;
+      const size_t orow = (size_t)(row0 + r) * a.ldo;
+      if constexpr (FC1) {
+        const float hv = silu_f32(v0[i]) * v1[i];
+        const size_t col = (size_t)(nb0 / 2 + c) * kTileN + m;
+        if constexpr (MX) static_cast<float*>(a.out)[orow + col] = hv;
+        else static_cast<uint16_t*>(a.out)[orow + col] = f32_to_bf16_rne(hv);
+      } else {
+        static_cast<float*>(a.out)[orow + (size_t)(nb0 + c) * kTileN + m] = v0[i];
+      }
+    }
+  }
+}
 
 #ifndef MOE_FUSED_WAVES
 #define MOE_FUSED_WAVES 3
@@ -302,7 +367,7 @@ hipError_t launch_fused_decode(const FcArgs& f1, const FcArgs& f2, const int32_t
   p.gen = gen;
   p.spin_ticks = spin_ticks;
   // the K split of each matrix is the stand-alone kernels' (a function of K alone)
-  const bool ks1 = f1.mat.kb >= kKsplit4Blocks, ks2 = f2.mat.kb >= kKsplit4Blocks;
+  const bool ks1 = dec_ksplit(f1.mat.kb) == 4, ks2 = dec_ksplit(f2.mat.kb) == 4;
   const int R = T * k;
   const int tiles = R / kBM + min(E, R);
   const int items = tiles * (f1.mat.nb / (kNBW * (ks1 ? 1 : 2)) + f2.mat.nb / (kNBW * (ks2 ? 1 : 2))) +

@@ -342,13 +342,28 @@ moe_status forward_with_layout(moe_mxfp4_plan_s* p, const Layout& L, const uint1
   const int bm = prefill ? moe::prefill_rows(T, L.k, L.E) : prefill_mx ? moe::kPrefillMxRows : moe::kBM;
   const int tiles_max = R / bm + (L.E < R ? L.E : R);
 
+  moe::FcArgs f1, f2;
+  fc_args(p, L, ws, ro, hidden, T, &f1, &f2);
+  if (!mx && R <= moe::kPerRouteMaxRoutes) {
+    // The smallest batches: two launches, no route stage.  FC1 runs one tile
+    // per route (h row f), FC2 sums each token's routes in its epilogue.
+    f1.route_ids = f2.route_ids = topk_ids;
+    f1.num_experts = f2.num_experts = L.E;
+    REC(0);
+    REC(1);
+    CHK(moe::launch_fc1_bf16_per_route(f1, R, stream), "FC1 launch");
+    REC(2);
+    CHK(moe::launch_fc2_sum_per_route(f2, topk_weights, T, L.H, acc_fp32, out_bf16, stream), "FC2 launch");
+    REC(3);
+    REC(4);
+    return ok();
+  }
+
   REC(0);
   CHK(moe::launch_route(L, topk_ids, T, ro, bm, stream), "route launch");
   if (mx) CHK(moe::launch_quant_bf16(hidden, T, L.H, ws + L.ws_xq, ws + L.ws_xs, stream), "x quant launch");
   REC(1);
 
-  moe::FcArgs f1, f2;
-  fc_args(p, L, ws, ro, hidden, T, &f1, &f2);
   if (prefill) CHK(moe::launch_fc1_prefill(f1, bm, tiles_max, stream), "FC1 launch");
   else if (prefill_mx) CHK(moe::launch_fc1_prefill_mx(f1, tiles_max, stream), "FC1 launch");
   else CHK(mx ? moe::launch_fc1_mx(f1, tiles_max, T, stream) : moe::launch_fc1_bf16(f1, tiles_max, T, stream),

@@ -115,12 +115,22 @@ struct FcArgs {
   uint8_t* out_codes;       // MXFP8 prefill FC1: h as E4M3 codes [R,I] (instead of fp32 `out`)
   uint8_t* out_scales;      // ... and its E8M0 bytes [R,I/32]
   int32_t* sched;           // bf16 prefill: kXcds work counters of this launch, zero on entry
+  const int32_t* route_ids; // per-route decode kernels: topk_ids [T*k] (the tile of route f is ids[f])
+  int32_t num_experts;      // ... ids outside [0, num_experts) get no tile
 };
 // `tokens` (the batch size) only picks a schedule; results do not depend on it.
 hipError_t launch_fc1_bf16(const FcArgs& a, int tiles_max, int tokens, hipStream_t stream);
 hipError_t launch_fc2_bf16(const FcArgs& a, int tiles_max, int tokens, hipStream_t stream);
 hipError_t launch_fc1_mx(const FcArgs& a, int tiles_max, int tokens, hipStream_t stream);
 hipError_t launch_fc2_mx(const FcArgs& a, int tiles_max, int tokens, hipStream_t stream);
+// Smallest bf16 batches (routes <= kPerRouteMaxRoutes): no route stage.  FC1
+// runs one tile per route (h row f for route f); FC2 runs over every valid
+// route for a block of output columns per workgroup and sums each token's
+// routes in slot order in its epilogue, writing acc and out itself.
+constexpr int kPerRouteMaxRoutes = 64;
+hipError_t launch_fc1_bf16_per_route(const FcArgs& a, int routes, hipStream_t stream);
+hipError_t launch_fc2_sum_per_route(const FcArgs& a, const float* weights, int32_t T, int32_t H, float* acc,
+                                    uint16_t* out, hipStream_t stream);
 
 // Prefill (MFMA-bound) FC kernels over bm-row tiles, bm in {64, 128}; bf16 path
 // (needs N % 256 == 0).  Persistent: `sched` holds the launch's work counters.

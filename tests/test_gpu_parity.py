@@ -448,15 +448,17 @@ def test_repeat_runs_identical_and_inputs_untouched(mid):
 
 @pytest.mark.parametrize("act", ["bf16", "mxfp8"])
 def test_small_and_large_decode_schedules_give_the_same_bits(act):
-    """16 tokens take the small-batch decode schedules, 17 the large ones:
-    a row's sums do not depend on the schedule (the K split is fixed), so the
-    first 16 rows agree bit for bit.  Also: a token with no valid route, and a
-    batch with none at all (no tile; the outputs still written, +0 over the
-    NaN fill)."""
-    case = W.make_case("fold", W.LayerShape(17, 256, 128, 8, 8, 2), 77, routing="uniform", invalid_frac=0.2,
+    """16 tokens take the small-batch decode schedules, 17 the large ones
+    (top-8 over 16 experts: more routes than the per-route path takes, fewer
+    than the prefill kernels need): a row's sums do not depend on the schedule
+    (the K split is fixed), so the first 16 rows agree bit for bit.  Also: a
+    token with no valid route, and a batch with none at all (no tile; the
+    outputs still written, +0 over the NaN fill) -- and 8 tokens (64 routes,
+    the per-route path) agree with the first 8 rows too."""
+    case = W.make_case("fold", W.LayerShape(17, 256, 128, 16, 20, 8), 77, routing="uniform", invalid_frac=0.2,
                        act=act)
     ids_np = case.topk_ids.copy()
-    ids_np[3] = [-1, 9]                          # token 3: no valid route (E = 8)
+    ids_np[3] = [-1, 17, 19, 16, -1, 18, 17, -1]  # token 3: no valid route (E = 16)
     say(f"small vs large decode schedules ({act})")
     plan, _ = G.make_plan(case)
     x = G.to_dev(case.hidden_bits).view(torch.bfloat16)
@@ -476,9 +478,14 @@ def test_small_and_large_decode_schedules_give_the_same_bits(act):
     out16, acc16 = run(16, ids)
     np.testing.assert_array_equal(G.bf16_bits(out16), G.bf16_bits(out17)[:16])
     np.testing.assert_array_equal(acc16.cpu().numpy(), acc17.cpu().numpy()[:16])
+    out8, acc8 = run(8, ids)
+    np.testing.assert_array_equal(G.bf16_bits(out8), G.bf16_bits(out17)[:8])
+    np.testing.assert_array_equal(acc8.cpu().numpy(), acc17.cpu().numpy()[:8])
     assert not G.bf16_bits(out16)[3].any() and not acc16[3].cpu().numpy().view(np.uint32).any()
     none = G.to_dev(np.full_like(ids_np, -1))
     out, acc = run(5, none)
+    assert not G.bf16_bits(out).any() and not acc.cpu().numpy().view(np.uint32).any()
+    out, acc = run(12, none)
     assert not G.bf16_bits(out).any() and not acc.cpu().numpy().view(np.uint32).any()
 
 
