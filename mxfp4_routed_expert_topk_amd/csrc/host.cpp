@@ -61,7 +61,7 @@ bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) !
 
 constexpr int32_t kMaxDim = moe::kMaxDimension;
 constexpr int32_t kMaxExperts = 1024;
-constexpr int32_t kMaxTopK = 32;
+constexpr int32_t kMaxTopK = moe::kMaxTopK;
 constexpr int64_t kMaxRoutes = 262144;
 
 moe_status check_config(const moe_mxfp4_config* c) {
