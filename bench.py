@@ -363,14 +363,14 @@ class Batches:
 
 
 # FC1 kernel source of each workload (the counter records hash it with the shared header)
-FC1_SOURCE = {"decode": "gemm.hip", "prefill1536": "gemm_prefill.hip", "fusedsum4096": "gemm_prefill.hip",
-              "mxfp8x4096": "gemm_prefill_mx.hip"}
+FC1_SOURCE = {"decode": ("gemm.hip", "dec_core.h"), "prefill1536": ("gemm_prefill.hip",),
+              "fusedsum4096": ("gemm_prefill.hip",), "mxfp8x4096": ("gemm_prefill_mx.hip",)}
 PREFILL = {"prefill1536": 2, "fusedsum4096": 3, "mxfp8x4096": 4}
 
 
 def source_hash(workload):
     csrc = os.path.join(ROOT, "mxfp4_routed_expert_topk_amd", "csrc")
-    src = b"".join(open(os.path.join(csrc, f), "rb").read() for f in (FC1_SOURCE[workload], "moe_internal.h"))
+    src = b"".join(open(os.path.join(csrc, f), "rb").read() for f in FC1_SOURCE[workload] + ("moe_internal.h",))
     return hashlib.sha256(src).hexdigest()
 
 
@@ -541,7 +541,7 @@ def main():
         "bound": "hbm", "achieved": round(fc1_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
         "frac": round(fc1_gbs / HBM_PEAK_GBS, 4),
         "traffic": counter_traffic("decode", "decode_m128") if args.m == 128 else None,
-        "kernel": "fc_dec<true,false,4,4,2> (FC1, bf16, 16-row tiles)", "kernel_us": round(fc1_us, 2),
+        "kernel": "fc_dec<true,false,4,4,2,false> (FC1, bf16, 16-row tiles)", "kernel_us": round(fc1_us, 2),
         "alg_bytes_per_launch": int(r["fc1_bytes"])}
     if ceil:
         line["roofline"]["measured_peak"] = ceil["hbm_read_nt_gbs"]

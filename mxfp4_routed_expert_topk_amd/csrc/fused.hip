@@ -108,9 +108,6 @@ __device__ __forceinline__ void dec_item(const FcArgs& a, int2 td, int group) {
   }
 }
 
-#ifndef MOE_FUSED_WAVES
-#define MOE_FUSED_WAVES 3
-#endif
 constexpr int kThreads = 4 * kWave;
 constexpr int kNBW = 2;                                // weight row blocks per wave and item
 constexpr int kP = 3;                                  // K blocks loaded ahead
@@ -169,7 +166,7 @@ __device__ bool poll(const uint32_t* c, uint32_t target, const FusedArgs& p) {
 }
 
 template <int KS1, int KS2>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(MOE_FUSED_WAVES, MOE_FUSED_WAVES)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3)))
 void fused_decode(FusedArgs p) {
   __shared__ int s_cnt[1024];                       // route scratch
   __shared__ int l_counts[1024], l_offsets[1025], l_perm[kFusedMaxRoutes], l_rowpos[kFusedMaxRoutes];

@@ -20,10 +20,6 @@
 // lgkmcnt(0) at their first use; in this order that wait only ever covers
 // reads that are a full step old.
 //
-// A build with MOE_PREFILL_WN=8 runs eight waves over 512 columns (one
-// workgroup per CU, a third less copying per MFMA); measured slower than two
-// four-wave workgroups per CU, so not the default.
-//
 // MFMA K order: in the stage covering K [64q, 64q+64) of a 128-K column block
 // (q = 0, 1), step s (16 K) of lane l (column n = l%32, half h = l/32)
 // multiplies K = 64q + 32h + 8s + [0, 8): for the weights that is dword s of
@@ -46,12 +42,9 @@
 // and, once the chunk is done, items left in the other chunks.  Under skewed
 // (Zipf) routing the chunks' work differs by tens of percent -- an XCD whose
 // chunk holds the most popular experts' full tiles would otherwise finish
-// last while the others idle.  Within a chunk, items run in groups of kTileGroup consecutive tiles
-// as (group, slice, tile in group): the tiles of a group that belong to one
-// expert -- an expert with many rows has many consecutive tiles -- read the
-// same weight slice at the same time and share it in L2, while the slices of
-// one tile still fall within one XCD's concurrent workgroups and share the
-// tile's activation rows.
+// last while the others idle.  Within a chunk items run tile by tile, the
+// slices of one tile consecutively: they fall within one XCD's concurrent
+// workgroups and share the tile's activation rows in its L2.
 #include <algorithm>
 
 #include "moe_internal.h"
@@ -66,10 +59,6 @@ typedef __attribute__((address_space(1))) void glob_void_t;
 
 constexpr int kStageK = 64;              // K per pipeline stage (half a repacked tile)
 constexpr int kHalfTile = kTileBytes / 2;
-#ifndef MOE_PREFILL_TILE_GROUP
-#define MOE_PREFILL_TILE_GROUP 1
-#endif
-constexpr int kTileGroup = MOE_PREFILL_TILE_GROUP;   // tiles sharing a weight slice in flight
 
 // Workgroup shape: W waves side by side over the columns (64 each, four
 // 16-column row blocks), every wave over all BM rows.  One pipeline stage
@@ -252,11 +241,11 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// W waves side by side: each owns all BM rows x one 64-column group, so every
-// weight fragment is dequantised once per workgroup.  W = 4: two workgroups
-// per CU.  W = 8: 512 columns per workgroup, one per CU -- each staged
-// activation row serves twice the columns, but all eight waves meet at every
-// stage barrier with no second workgroup to fill the gaps.
+// W = 4 waves side by side: each owns all BM rows x one 64-column group, so
+// every weight fragment is dequantised once per workgroup; two workgroups per
+// CU.  (Eight waves over 512 columns, one workgroup per CU, give each staged
+// activation row twice the columns but meet at every stage barrier with no
+// second workgroup to fill the gaps: measured slower.)
 template <bool FC1, int BM, int W>
 __global__ __launch_bounds__(W * kWave)
 __attribute__((amdgpu_waves_per_eu(Cfg<BM, W>::kWavesPerSimd, Cfg<BM, W>::kWavesPerSimd)))
@@ -266,7 +255,7 @@ void fc_pre(FcArgs a, int slices) {
   __shared__ int s_item;
 
   const int ntiles = *a.tile_count;
-  const int total = (ntiles + kTileGroup - 1) / kTileGroup * kTileGroup * slices;   // whole groups
+  const int total = ntiles * slices;
   const int chunk = (total + kXcds - 1) / kXcds;
   const int xcd = blockIdx.x % kXcds;
   const bool leader = threadIdx.x == 0;
@@ -297,8 +286,7 @@ void fc_pre(FcArgs a, int slices) {
   }
 }
 
-// Item w of the work list: (tile, column slice) in groups of kTileGroup
-// consecutive tiles as (group, slice, tile in group).
+// Item w of the work list: (tile w / slices, column slice w % slices).
 // Kept out of line: inlined into the persistent loop, the item needs more than
 // 256 VGPRs and the spill reloads in its epilogue wait (vmcnt(0)) for every
 // output store already issued.  After the K loop the leader takes the next
@@ -310,9 +298,7 @@ __device__ __noinline__ void fc_pre_item(const FcArgs& a, uint8_t* smem, int sli
   using C = Cfg<BM, W>;
   constexpr int MI = C::MI;
   constexpr int NJ = 2;                      // 32-column MFMA blocks per wave (its 64 columns)
-  const int per_group = kTileGroup * slices;
-  const int grp = w / per_group, rem = w - grp * per_group;
-  const int slice = rem / kTileGroup, tile = grp * kTileGroup + (rem - slice * kTileGroup);
+  const int tile = w / slices, slice = w - tile * slices;
   if (tile >= ntiles) {
     lds_barrier();   // every wave has read s_item before it is rewritten
     if (threadIdx.x == 0) *s_item = atomicAdd(counter, 1);
@@ -355,18 +341,12 @@ __device__ __noinline__ void fc_pre_item(const FcArgs& a, uint8_t* smem, int sli
       for (int i = 0; i < 16; ++i) acc[mi][nj][i] = 0.f;
 
   const int S = 2 * M.kb;    // stages
-  if constexpr (MI == 4) {
-    switch (live) {
-      case 1: k_loop<C, 1>(smem, src, S, wave, lane, acc); break;
-      case 2: k_loop<C, 2>(smem, src, S, wave, lane, acc); break;
-      case 3: k_loop<C, 3>(smem, src, S, wave, lane, acc); break;
-      default: k_loop<C, 4>(smem, src, S, wave, lane, acc); break;
-    }
-  } else {
-    switch (live) {
-      case 1: k_loop<C, 1>(smem, src, S, wave, lane, acc); break;
-      default: k_loop<C, 2>(smem, src, S, wave, lane, acc); break;
-    }
+  static_assert(MI == 4, "128-row tiles");
+  switch (live) {
+    case 1: k_loop<C, 1>(smem, src, S, wave, lane, acc); break;
+    case 2: k_loop<C, 2>(smem, src, S, wave, lane, acc); break;
+    case 3: k_loop<C, 3>(smem, src, S, wave, lane, acc); break;
+    default: k_loop<C, 4>(smem, src, S, wave, lane, acc); break;
   }
   const int next = threadIdx.x == 0 ? atomicAdd(counter, 1) : 0;
   const int n32 = lane & 31, h = lane >> 5;
@@ -400,15 +380,11 @@ __device__ __noinline__ void fc_pre_item(const FcArgs& a, uint8_t* smem, int sli
   if (threadIdx.x == 0) *s_item = next;
 }
 
-#ifndef MOE_PREFILL_WN
-#define MOE_PREFILL_WN 4
-#endif
-
-template <bool FC1, int BM, int W>
+template <bool FC1>
 hipError_t launch_cfg(const FcArgs& a, int tiles_max, hipStream_t stream) {
-  using C = Cfg<BM, W>;
+  using C = Cfg<kPrefillRows, 4>;
   const int slices = a.mat.nb / C::kBlocks;
-  const long long items = (long long)((tiles_max + kTileGroup - 1) / kTileGroup * kTileGroup) * slices;
+  const long long items = (long long)tiles_max * slices;
   // as many workgroups as the device holds at once (kPerCU per CU), a multiple
   // of the XCD count, and no more than there can be items
   int dev = 0, cus = 0;
@@ -417,37 +393,13 @@ hipError_t launch_cfg(const FcArgs& a, int tiles_max, hipStream_t stream) {
   if (e != hipSuccess) return e;
   const long long resident = (long long)cus * C::kPerCU / kXcds * kXcds;
   const long long grid = std::max<long long>(kXcds, std::min(resident, (items + kXcds - 1) / kXcds * kXcds));
-  hipLaunchKernelGGL((fc_pre<FC1, BM, W>), dim3((unsigned)grid), dim3(W * kWave), 0, stream, a, slices);
+  hipLaunchKernelGGL((fc_pre<FC1, kPrefillRows, 4>), dim3((unsigned)grid), dim3(4 * kWave), 0, stream, a, slices);
   return hipGetLastError();
-}
-
-template <bool FC1, int BM>
-hipError_t launch_pre(const FcArgs& a, int tiles_max, hipStream_t stream) {
-  // 512-column workgroups where chosen and N allows (N a multiple of 512), else 256
-  if constexpr (BM == 128 && MOE_PREFILL_WN == 8) {
-    if (a.mat.nb % Cfg<BM, 8>::kBlocks == 0) return launch_cfg<FC1, BM, 8>(a, tiles_max, stream);
-  }
-  return launch_cfg<FC1, BM, 4>(a, tiles_max, stream);
 }
 
 }  // namespace
 
-#ifndef MOE_PREFILL_BM
-#define MOE_PREFILL_BM 128
-#endif
-
-int prefill_rows(int tokens, int top_k, int experts) {
-  // The tile height only changes the schedule (a row's K order is fixed); 128-row
-  // tiles with all-padding 32-row blocks skipped serve every batch here.
-  (void)tokens; (void)top_k; (void)experts;
-  return MOE_PREFILL_BM;
-}
-
-hipError_t launch_fc1_prefill(const FcArgs& a, int bm, int tiles_max, hipStream_t s) {
-  return bm == 128 ? launch_pre<true, 128>(a, tiles_max, s) : launch_pre<true, 64>(a, tiles_max, s);
-}
-hipError_t launch_fc2_prefill(const FcArgs& a, int bm, int tiles_max, hipStream_t s) {
-  return bm == 128 ? launch_pre<false, 128>(a, tiles_max, s) : launch_pre<false, 64>(a, tiles_max, s);
-}
+hipError_t launch_fc1_prefill(const FcArgs& a, int tiles_max, hipStream_t s) { return launch_cfg<true>(a, tiles_max, s); }
+hipError_t launch_fc2_prefill(const FcArgs& a, int tiles_max, hipStream_t s) { return launch_cfg<false>(a, tiles_max, s); }
 
 }  // namespace moe

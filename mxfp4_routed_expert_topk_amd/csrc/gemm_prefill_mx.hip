@@ -50,15 +50,8 @@ typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 
 constexpr int kRows = kPrefillMxRows;       // rows per tile
-#ifndef MOE_MX_NBW
-#define MOE_MX_NBW 4
-#endif
-constexpr int kNBW = MOE_MX_NBW;            // row blocks (16 output columns each) per wave: 2 or 4
-static_assert(kNBW == 2 || kNBW == 4, "gate/up pairs of row blocks per wave");
-#ifndef MOE_MX_DEPTH
-#define MOE_MX_DEPTH 2
-#endif
-constexpr int kDepth = MOE_MX_DEPTH;        // stages loaded ahead of the one multiplied
+constexpr int kNBW = 4;                     // row blocks (16 output columns each) per wave
+constexpr int kDepth = 2;                   // stages loaded ahead of the one multiplied
 constexpr int kBufs = kDepth + 1;           // LDS stage buffers
 constexpr int kStageA = kRows * kTileK;       // 128 rows x 128 E4M3
 constexpr int kStageBytes = kStageA + kRows * 4;   // + each row's four E8M0 bytes of the stage

@@ -339,7 +339,7 @@ moe_status forward_with_layout(moe_mxfp4_plan_s* p, const Layout& L, const uint1
   const bool large = (int64_t)R >= 16LL * L.E && L.H % 256 == 0;
   const bool prefill = large && !mx;
   const bool prefill_mx = large && mx && (int64_t)T * L.H < (1LL << 31) && (int64_t)R * L.I < (1LL << 31);
-  const int bm = prefill ? moe::prefill_rows(T, L.k, L.E) : prefill_mx ? moe::kPrefillMxRows : moe::kBM;
+  const int bm = prefill ? moe::kPrefillRows : prefill_mx ? moe::kPrefillMxRows : moe::kBM;
   const int tiles_max = R / bm + (L.E < R ? L.E : R);
 
   moe::FcArgs f1, f2;
@@ -364,7 +364,7 @@ moe_status forward_with_layout(moe_mxfp4_plan_s* p, const Layout& L, const uint1
   if (mx) CHK(moe::launch_quant_bf16(hidden, T, L.H, ws + L.ws_xq, ws + L.ws_xs, stream), "x quant launch");
   REC(1);
 
-  if (prefill) CHK(moe::launch_fc1_prefill(f1, bm, tiles_max, stream), "FC1 launch");
+  if (prefill) CHK(moe::launch_fc1_prefill(f1, tiles_max, stream), "FC1 launch");
   else if (prefill_mx) CHK(moe::launch_fc1_prefill_mx(f1, tiles_max, stream), "FC1 launch");
   else CHK(mx ? moe::launch_fc1_mx(f1, tiles_max, T, stream) : moe::launch_fc1_bf16(f1, tiles_max, T, stream),
            "FC1 launch");
@@ -373,7 +373,7 @@ moe_status forward_with_layout(moe_mxfp4_plan_s* p, const Layout& L, const uint1
   if (mx && !prefill_mx)   // the MXFP8 prefill FC1 requantises h itself
     CHK(moe::launch_quant_f32(reinterpret_cast<const float*>(ws + L.ws_h), ro.offsets + L.E, T * L.k, L.I,
                               ws + L.ws_hq, ws + L.ws_hs, stream), "h quant launch");
-  if (prefill) CHK(moe::launch_fc2_prefill(f2, bm, tiles_max, stream), "FC2 launch");
+  if (prefill) CHK(moe::launch_fc2_prefill(f2, tiles_max, stream), "FC2 launch");
   else if (prefill_mx) CHK(moe::launch_fc2_prefill_mx(f2, tiles_max, stream), "FC2 launch");
   else CHK(mx ? moe::launch_fc2_mx(f2, tiles_max, T, stream) : moe::launch_fc2_bf16(f2, tiles_max, T, stream),
            "FC2 launch");

@@ -135,11 +135,11 @@ hipError_t launch_fc1_bf16_per_route(const FcArgs& a, int routes, hipStream_t st
 hipError_t launch_fc2_sum_per_route(const FcArgs& a, const float* weights, int32_t T, int32_t H, float* acc,
                                     uint16_t* out, hipStream_t stream);
 
-// Prefill (MFMA-bound) FC kernels over bm-row tiles, bm in {64, 128}; bf16 path
-// (needs N % 256 == 0).  Persistent: `sched` holds the launch's work counters.
-int prefill_rows(int tokens, int top_k, int experts);
-hipError_t launch_fc1_prefill(const FcArgs& a, int bm, int tiles_max, hipStream_t stream);
-hipError_t launch_fc2_prefill(const FcArgs& a, int bm, int tiles_max, hipStream_t stream);
+// Prefill (MFMA-bound) FC kernels over 128-row tiles, bf16 path (needs
+// N % 256 == 0).  Persistent: `sched` holds the launch's work counters.
+constexpr int kPrefillRows = 128;
+hipError_t launch_fc1_prefill(const FcArgs& a, int tiles_max, hipStream_t stream);
+hipError_t launch_fc2_prefill(const FcArgs& a, int tiles_max, hipStream_t stream);
 // Prefill FC kernels of the MXFP8 path over 128-row tiles (needs N % 256 == 0
 // and A plus its scales addressable with 32-bit offsets).  FC1 writes h already
 // requantised to MXFP8 (out_codes / out_scales) by the rule launch_quant_f32

@@ -116,10 +116,7 @@ __global__ __launch_bounds__(kThreads) void route_fused(const int32_t* ids, int 
   scatter_chunk(ids, R, E, 0, s_off, wcnt, o);
 }
 
-#ifndef MOE_SMALL_ROUTES
-#define MOE_SMALL_ROUTES 64
-#endif
-constexpr int kSmallRoutes = MOE_SMALL_ROUTES;   // routes the one-wave kernel takes (route_wave.h)
+constexpr int kSmallRoutes = 64;   // routes the one-wave kernel takes (route_wave.h)
 
 // One wave: everything for R <= kSmallRoutes (decode batches).
 __global__ __launch_bounds__(kWave) void route_small(const int32_t* ids, int R, int E, int bm, RouteOut o) {
