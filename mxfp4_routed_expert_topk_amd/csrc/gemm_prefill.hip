@@ -87,6 +87,15 @@ struct Cfg {
   static_assert(nA * 8 * W == BM && nB * 2 * W == kBlocks, "copies split evenly over the waves");
 };
 
+// A value every lane holds alike, moved to a scalar register.
+__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+template <class T>
+__device__ __forceinline__ T* uni(T* p) {
+  const uint64_t u = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u), hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+  return reinterpret_cast<T*>(((uint64_t)hi << 32) | lo);
+}
+
 // LDS position of K chunk c (0..7) in staged activation row r.
 __device__ __forceinline__ int swz(int c, int r) { return c ^ (r & 7) ^ ((r >> 3) & 1); }
 
@@ -170,11 +179,11 @@ __device__ __forceinline__ void k_loop(uint8_t* smem, const StageSrc<C>& src, in
     const bool refill = st + 2 < S;
     const int sh = ((st >> 1) & 3) * 8;
     u32x4_t bc[NJ];
-    float bs[NJ];
+    uint32_t sraw[NJ];
 #pragma unroll
     for (int nj = 0; nj < NJ; ++nj) {
+      sraw[nj] = *reinterpret_cast<const uint32_t*>(cur + soff + 2 * nj * 32 * 4);
       bc[nj] = *reinterpret_cast<const u32x4_t*>(cur + C::kA + boff + 2 * nj * kHalfTile);
-      bs[nj] = e8m0_to_f32((*reinterpret_cast<const uint32_t*>(cur + soff + 2 * nj * 32 * 4) >> sh) & 0xFFu);
     }
     // Step s+1's activation fragments are read while step s multiplies.  Per
     // step: the dequantised weights and the first MFMA (the compiler waits
@@ -188,6 +197,13 @@ __device__ __forceinline__ void k_loop(uint8_t* smem, const StageSrc<C>& src, in
 #pragma unroll
     for (int mi = 0; mi < LIVE; ++mi)
       Ac[mi] = *reinterpret_cast<const bf16x8_t*>(arow + mi * 32 * (kStageK * 2) + swz(4 * h, n32) * 16);
+    // every read of the stage head is issued before the first of them is used
+    // (left to itself the compiler waits for the scale bytes before issuing
+    // the other reads: two LDS round trips at every stage head)
+    __builtin_amdgcn_sched_barrier(0);
+    float bs[NJ];
+#pragma unroll
+    for (int nj = 0; nj < NJ; ++nj) bs[nj] = e8m0_to_f32((sraw[nj] >> sh) & 0xFFu);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       bf16x8_t B[NJ];
@@ -298,20 +314,33 @@ __device__ __noinline__ void fc_pre_item(const FcArgs& a, uint8_t* smem, int sli
   using C = Cfg<BM, W>;
   constexpr int MI = C::MI;
   constexpr int NJ = 2;                      // 32-column MFMA blocks per wave (its 64 columns)
-  const int tile = w / slices, slice = w - tile * slices;
-  if (tile >= ntiles) {
+  // Everything that describes the item is the same in every lane: taken
+  // through readfirstlane, it lives in scalar registers and the stage loop's
+  // control is a scalar branch (arguments of a function call arrive in vector
+  // registers, and so does what is loaded through them).
+  slices = uni(slices);
+  const int tile = uni(w) / slices, slice = uni(w) - tile * slices;
+  if (tile >= uni(ntiles)) {
     lds_barrier();   // every wave has read s_item before it is rewritten
     if (threadIdx.x == 0) *s_item = atomicAdd(counter, 1);
     return;
   }
   const int2 td = a.tiles[tile];
-  const int e = td.x, row0 = td.y;
-  const int rows = min(BM, a.offsets[e + 1] - row0);
-  const MatLayout M = a.mat;
+  const int e = uni(td.x), row0 = uni(td.y);
+  const int rows = uni(min(BM, a.offsets[e + 1] - row0));
+  MatLayout M = a.mat;
+  M.nb = uni(M.nb);
+  M.kb = uni(M.kb);
+  M.kb4 = uni(M.kb4);
   const int t = threadIdx.x, lane = t & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int wave = uni(t >> 6);
   const int nb0 = slice * C::kBlocks;
   const int live = (rows + 31) >> 5;         // 32-row blocks holding a row, 1..MI
+  const uint8_t* const codes = uni(a.codes);
+  const uint8_t* const scales = uni(a.scales);
+  const uint8_t* const act = uni(static_cast<const uint8_t*>(a.a));
+  const int lda = uni(a.lda), top_k = uni(a.top_k), ldo = uni(a.ldo);
+  void* const out = uni(a.out);
 
   StageSrc<C> src;
   // activation chunks this lane copies: copy i = wave + W j writes rows
@@ -321,15 +350,15 @@ __device__ __noinline__ void fc_pre_item(const FcArgs& a, uint8_t* smem, int sli
   for (int j = 0; j < C::nA; ++j) {
     const int r = 8 * (wave + W * j) + (lane >> 3);
     const int rr = min(r, rows - 1);
-    const int ar = FC1 ? a.perm[row0 + rr] / a.top_k : row0 + rr;
-    src.a[j] = static_cast<const uint8_t*>(a.a) + (size_t)ar * a.lda * 2 + swz(lane & 7, r) * 16;
+    const int ar = FC1 ? a.perm[row0 + rr] / top_k : row0 + rr;
+    src.a[j] = act + (size_t)ar * lda * 2 + swz(lane & 7, r) * 16;
   }
   // codes / scales this lane copies: row block 2(wave + W j) + lane/32, chunk or dword lane%32
 #pragma unroll
   for (int j = 0; j < C::nB; ++j) {
     const int blk = nb0 + 2 * (wave + W * j) + (lane >> 5);
-    src.b[j] = a.codes + ((size_t)e * M.nb + blk) * M.kb * kTileBytes + (lane & 31) * 16;
-    src.s[j] = a.scales + ((size_t)e * M.nb + blk) * M.kb4 * kScaleGroupBytes + (lane & 31) * 4;
+    src.b[j] = codes + ((size_t)e * M.nb + blk) * M.kb * kTileBytes + (lane & 31) * 16;
+    src.s[j] = scales + ((size_t)e * M.nb + blk) * M.kb4 * kScaleGroupBytes + (lane & 31) * 4;
   }
 
   f32x16_t acc[MI][NJ];
@@ -366,12 +395,12 @@ __device__ __noinline__ void fc_pre_item(const FcArgs& a, uint8_t* smem, int sli
           const float u = __shfl_xor(v, 16, kWave);
           if (n32 < 16 && r < rows) {
             const int j = (nb0 + wave * (2 * NJ) + 2 * nj) >> 1;
-            static_cast<uint16_t*>(a.out)[(size_t)(row0 + r) * a.ldo + j * kTileN + n32] =
+            static_cast<uint16_t*>(out)[(size_t)(row0 + r) * ldo + j * kTileN + n32] =
                 f32_to_bf16_rne(silu_f32(v) * u);
           }
         } else {
           if (r < rows)
-            static_cast<float*>(a.out)[(size_t)(row0 + r) * a.ldo +
+            static_cast<float*>(out)[(size_t)(row0 + r) * ldo +
                                        (size_t)(nb0 + wave * (2 * NJ) + 2 * nj) * kTileN + n32] = v;
         }
       }
