@@ -46,6 +46,7 @@
 // slices of one tile consecutively: they fall within one XCD's concurrent
 // workgroups and share the tile's activation rows in its L2.
 #include <algorithm>
+#include <type_traits>
 
 #include "moe_internal.h"
 
@@ -59,6 +60,7 @@ typedef __attribute__((address_space(1))) void glob_void_t;
 
 constexpr int kStageK = 64;              // K per pipeline stage (half a repacked tile)
 constexpr int kHalfTile = kTileBytes / 2;
+constexpr int kDepth = 3;               // stages loaded ahead
 
 // Workgroup shape: W waves side by side over the columns (64 each, four
 // 16-column row blocks), every wave over all BM rows.  One pipeline stage
@@ -243,6 +245,131 @@ __device__ __forceinline__ void k_loop(uint8_t* smem, const StageSrc<C>& src, in
   }
 }
 
+// Stages ring_pass runs: s0 + P .. s0 + N - 1 that lie below s0 + n, ring slots P .. N - 1.
+template <int P, int N, class F>
+__device__ __forceinline__ void ring_pass(F& f, int s0, int n) {
+  if constexpr (P < N) {
+    if (P < n) {
+      f(std::integral_constant<int, P>{}, s0 + P);
+      ring_pass<P + 1, N>(f, s0, n);
+    }
+  }
+}
+
+// The K loop with the weights in registers: only the activation rows, which
+// the four waves share, go through LDS (a ring of D + 1 stages); each wave
+// loads its own weight chunks -- the 16 code bytes a lane multiplies in each
+// of its two 32-column blocks and the dwords holding their E8M0 bytes --
+// straight into a ring of D + 1 register sets, D stages ahead.  Every stage
+// issues the same group of loads (past the last stage: activation copies of
+// the last stage again, into the slot no later stage reads, and weight loads
+// outside their buffer resource, which return zeros without a memory request),
+// so the wait before each stage counts them exactly and the compiler never
+// waits at the MFMAs for weights still in flight.
+template <class C, int LIVE, int D>
+__device__ __forceinline__ void k_loop_r(uint8_t* smem, const uint8_t* const (&srcA)[C::nA],
+                                         __amdgpu_buffer_rsrc_t rcode, __amdgpu_buffer_rsrc_t rscale,
+                                         const uint32_t (&coff)[2], const uint32_t (&soff)[2], int S, int wave,
+                                         int lane, f32x16_t (&acc)[C::MI][2]) {
+  constexpr int NJ = 2;
+  constexpr int W = C::W;
+  constexpr int NA = C::nA_live(LIVE);   // activation copies per wave and stage
+  constexpr int G = NA + 2 * NJ;         // loads per wave and stage
+  constexpr int R = D + 1;               // ring slots
+  constexpr uint32_t kPastEnd = 0x80000000u;
+  static_assert(R * C::kA * C::kPerCU <= 160 * 1024, "activation ring");
+  const int n32 = lane & 31, h = lane >> 5;
+  const int aoff = n32 * (kStageK * 2);
+  u32x4_t bc[R][NJ];
+  uint32_t sraw[R][NJ];
+
+  // loads [first, last) of stage st's group into ring slot `slot`
+  auto issue = [&](auto slot_c, int st, int first, int last) {
+    constexpr int slot = decltype(slot_c)::value;
+    const bool real = st < S;
+    const int sa = min(st, S - 1);
+    uint8_t* buf = smem + slot * C::kA;
+#pragma unroll
+    for (int c = 0; c < G; ++c) {
+      if (c < first || c >= last) continue;
+      if (c < NA) {
+        __builtin_amdgcn_global_load_lds((glob_void_t*)(srcA[c] + (size_t)sa * (kStageK * 2)),
+                                         (lds_void_t*)(buf + (wave + W * c) * 1024), 16, 0, 0);
+      } else if (c < NA + NJ) {
+        const int nj = c - NA;
+        bc[slot][nj] = __builtin_amdgcn_raw_buffer_load_b128(rcode, real ? coff[nj] : kPastEnd,
+                                                             real ? st * kHalfTile : 0, 0);
+      } else {
+        const int nj = c - NA - NJ;
+        sraw[slot][nj] = __builtin_amdgcn_raw_buffer_load_b32(rscale, real ? soff[nj] : kPastEnd,
+                                                              real ? (int)scale_off(st) : 0, 0);
+      }
+    }
+  };
+
+  auto run_stage = [&](auto pc, int st) {
+    constexpr int p = decltype(pc)::value;   // ring slot of stage st
+    constexpr int q = (p + D) % R;           // slot of stage st - 1, refilled with stage st + D
+    // this wave's group of stage st has landed (the D - 1 groups after it may
+    // still be in flight) and its LDS reads of stage st - 1 have returned; the
+    // barrier extends both to every wave
+    MOE_WAIT_VMCNT((D - 1) * G);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    const uint8_t* arow = smem + p * C::kA + aoff;
+    const int sh = ((st >> 1) & 3) * 8;
+    bf16x8_t Ac[LIVE], An[LIVE];
+#pragma unroll
+    for (int mi = 0; mi < LIVE; ++mi)
+      Ac[mi] = *reinterpret_cast<const bf16x8_t*>(arow + mi * 32 * (kStageK * 2) + swz(4 * h, n32) * 16);
+    float bs[NJ];
+#pragma unroll
+    for (int nj = 0; nj < NJ; ++nj) bs[nj] = e8m0_to_f32((sraw[p][nj] >> sh) & 0xFFu);
+    // per step as in k_loop: the first MFMA, the step's share of the loads of
+    // stage st + D, the next step's activation reads, the other MFMAs
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      bf16x8_t B[NJ];
+#pragma unroll
+      for (int nj = 0; nj < NJ; ++nj) B[nj] = dequant8(bc[p][nj][s], bs[nj]);
+      acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Ac[0], B[0], acc[0][0], 0, 0, 0);
+      issue(std::integral_constant<int, q>{}, st + D, s * G / 4, (s + 1) * G / 4);
+      if (s < 3) {
+#pragma unroll
+        for (int mi = 0; mi < LIVE; ++mi)
+          An[mi] =
+              *reinterpret_cast<const bf16x8_t*>(arow + mi * 32 * (kStageK * 2) + swz(4 * h + s + 1, n32) * 16);
+      }
+#pragma unroll
+      for (int mi = 0; mi < LIVE; ++mi)
+#pragma unroll
+        for (int nj = 0; nj < NJ; ++nj)
+          if (mi + nj > 0)
+            acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Ac[mi], B[nj], acc[mi][nj], 0, 0, 0);
+      if (s < 3) __builtin_amdgcn_sched_group_barrier(0x100, LIVE, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, NJ * LIVE - 1, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      if (s < 3) {
+#pragma unroll
+        for (int mi = 0; mi < LIVE; ++mi) Ac[mi] = An[mi];
+      }
+    }
+  };
+
+  // one group after another: the waits count whole groups in issue order
+  auto prologue = [&](auto pc, int st) {
+    issue(pc, st, 0, G);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  ring_pass<0, D>(prologue, 0, D);
+  int s0 = 0;
+  for (; s0 + R <= S; s0 += R) ring_pass<0, R>(run_stage, s0, R);
+  ring_pass<0, R - 1>(run_stage, s0, S - s0);   // the last S % R stages
+  // the copies past the end still write LDS: drained before the ring is reused
+  MOE_WAIT_VMCNT(0);
+}
+
 template <bool FC1, int BM, int W>
 __device__ __noinline__ void fc_pre_item(const FcArgs& a, uint8_t* smem, int slices, int ntiles, int w,
                                             int* s_item, int* counter);
@@ -267,7 +394,7 @@ __global__ __launch_bounds__(W * kWave)
 __attribute__((amdgpu_waves_per_eu(Cfg<BM, W>::kWavesPerSimd, Cfg<BM, W>::kWavesPerSimd)))
 void fc_pre(FcArgs a, int slices) {
   using C = Cfg<BM, W>;
-  __shared__ __align__(1024) uint8_t smem[3 * C::kBytes];
+  __shared__ __align__(1024) uint8_t smem[(kDepth + 1) * C::kA];
   __shared__ int s_item;
 
   const int ntiles = *a.tile_count;
@@ -342,23 +469,35 @@ __device__ __noinline__ void fc_pre_item(const FcArgs& a, uint8_t* smem, int sli
   const int lda = uni(a.lda), top_k = uni(a.top_k), ldo = uni(a.ldo);
   void* const out = uni(a.out);
 
-  StageSrc<C> src;
   // activation chunks this lane copies: copy i = wave + W j writes rows
   // 8i..8i+7 (128 bytes each); lane L fills row 8i + L/8 at position L%8 with
   // the K chunk c that the swizzle places there.
+  const uint8_t* srcA[C::nA];
 #pragma unroll
   for (int j = 0; j < C::nA; ++j) {
     const int r = 8 * (wave + W * j) + (lane >> 3);
     const int rr = min(r, rows - 1);
     const int ar = FC1 ? a.perm[row0 + rr] / top_k : row0 + rr;
-    src.a[j] = act + (size_t)ar * lda * 2 + swz(lane & 7, r) * 16;
+    srcA[j] = act + (size_t)ar * lda * 2 + swz(lane & 7, r) * 16;
   }
-  // codes / scales this lane copies: row block 2(wave + W j) + lane/32, chunk or dword lane%32
+  // the wave's four weight row blocks as buffer resources sized to them; lane
+  // (n32, h) multiplies 16-byte chunk (n32 % 16) + 16 h of each stage's half
+  // tile of row block 2 nj + n32 / 16, and the dword of the same index in the
+  // stage's half of the scale group
+  const uint32_t bstride = (uint32_t)M.kb * kTileBytes, sstride = (uint32_t)M.kb4 * kScaleGroupBytes;
+  const size_t blk0 = (size_t)e * M.nb + nb0 + wave * (2 * NJ);
+  const __amdgpu_buffer_rsrc_t rcode = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(codes) + blk0 * bstride, (short)0, (int)(2 * NJ * bstride), kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rscale = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(scales) + blk0 * sstride, (short)0, (int)(2 * NJ * sstride), kRsrcWord3);
+  uint32_t coff[NJ], soff[NJ];
+  {
+    const int lp = (lane & 15) + 16 * (lane >> 5), rb = (lane >> 4) & 1;
 #pragma unroll
-  for (int j = 0; j < C::nB; ++j) {
-    const int blk = nb0 + 2 * (wave + W * j) + (lane >> 5);
-    src.b[j] = codes + ((size_t)e * M.nb + blk) * M.kb * kTileBytes + (lane & 31) * 16;
-    src.s[j] = scales + ((size_t)e * M.nb + blk) * M.kb4 * kScaleGroupBytes + (lane & 31) * 4;
+    for (int nj = 0; nj < NJ; ++nj) {
+      coff[nj] = (uint32_t)(2 * nj + rb) * bstride + lp * 16;
+      soff[nj] = (uint32_t)(2 * nj + rb) * sstride + lp * 4;
+    }
   }
 
   f32x16_t acc[MI][NJ];
@@ -372,10 +511,10 @@ __device__ __noinline__ void fc_pre_item(const FcArgs& a, uint8_t* smem, int sli
   const int S = 2 * M.kb;    // stages
   static_assert(MI == 4, "128-row tiles");
   switch (live) {
-    case 1: k_loop<C, 1>(smem, src, S, wave, lane, acc); break;
-    case 2: k_loop<C, 2>(smem, src, S, wave, lane, acc); break;
-    case 3: k_loop<C, 3>(smem, src, S, wave, lane, acc); break;
-    default: k_loop<C, 4>(smem, src, S, wave, lane, acc); break;
+    case 1: k_loop_r<C, 1, kDepth>(smem, srcA, rcode, rscale, coff, soff, S, wave, lane, acc); break;
+    case 2: k_loop_r<C, 2, kDepth>(smem, srcA, rcode, rscale, coff, soff, S, wave, lane, acc); break;
+    case 3: k_loop_r<C, 3, kDepth>(smem, srcA, rcode, rscale, coff, soff, S, wave, lane, acc); break;
+    default: k_loop_r<C, 4, kDepth>(smem, srcA, rcode, rscale, coff, soff, S, wave, lane, acc); break;
   }
   const int next = threadIdx.x == 0 ? atomicAdd(counter, 1) : 0;
   const int n32 = lane & 31, h = lane >> 5;

@@ -55,7 +55,6 @@ constexpr int kDepth = 2;                   // stages loaded ahead of the one mu
 constexpr int kBufs = kDepth + 1;           // LDS stage buffers
 constexpr int kStageA = kRows * kTileK;       // 128 rows x 128 E4M3
 constexpr int kStageBytes = kStageA + kRows * 4;   // + each row's four E8M0 bytes of the stage
-constexpr int kRsrcWord3 = 0x00020000;        // raw buffer, 32-bit data format
 
 // vmcnt <= n with lgkmcnt 0 (every LDS read of the previous stage returned)
 #define MOE_WAIT_VM_LGKM(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | ((((n) >> 4) & 3) << 14))

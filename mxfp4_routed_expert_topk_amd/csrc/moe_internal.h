@@ -28,6 +28,7 @@ constexpr int kTileN = 16;          // rows per repacked tile
 constexpr int kTileK = 128;         // K per repacked tile
 constexpr int kTileBytes = 1024;    // codes per tile
 constexpr int kScaleGroupBytes = 256;
+constexpr int kRsrcWord3 = 0x00020000;   // buffer resource word 3: raw buffer, 32-bit data format
 constexpr int kRouteChunk = 1024;   // routes per route workgroup
 constexpr int kBM = 16;             // rows per FC tile (one MFMA M block)
 // K column blocks from which the decode kernels split K four ways (else two):
