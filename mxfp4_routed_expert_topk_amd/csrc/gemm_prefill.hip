@@ -60,33 +60,31 @@ typedef __attribute__((address_space(1))) void glob_void_t;
 
 constexpr int kStageK = 64;              // K per pipeline stage (half a repacked tile)
 constexpr int kHalfTile = kTileBytes / 2;
-constexpr int kDepth = 3;               // stages loaded ahead
+// Stages loaded ahead: the LDS ring holds kRingBytes of activation rows, so
+// tiles with fewer live rows keep more stages in flight (their K loop is bound
+// by the weight stream, not by the MFMAs).  A ring of D + 1 slots divides the
+// stage counts of the layer's two GEMMs (K / 64 = 112 and 32), which leaves no
+// stages to the loop's tail.
+constexpr int kRingBytes = 64 * 1024;
+template <int LIVE>
+constexpr int depth_for() { return LIVE <= 2 ? 7 : 3; }
+
 
 // Workgroup shape: W waves side by side over the columns (64 each, four
-// 16-column row blocks), every wave over all BM rows.  One pipeline stage
-// holds the BM activation rows of 64 K (bf16), the code half-tiles of the
-// workgroup's row blocks and their scale dwords; each wave copies an equal
-// share of it.
+// 16-column row blocks), every wave over all BM rows.
 template <int BM, int W_>
 struct Cfg {
   static constexpr int W = W_;
   static constexpr int kBlocks = 4 * W;                  // repacked row blocks per workgroup
-  static constexpr int kA = BM * kStageK * 2;            // activation rows
-  static constexpr int kB = kBlocks * kHalfTile;         // code half-tiles
-  static constexpr int kS = kBlocks * 32 * 4;            // scale dwords of the half
-  static constexpr int kBytes = kA + kB + kS;
-  static constexpr int nA = BM / 8 / W;                  // 1 KB copies of eight activation rows
-  static constexpr int nB = kBlocks / 2 / W;             // 1 KB copies of two code half-tiles
-  static constexpr int nS = nB;                          // 256 B copies of their scale dwords
+  static constexpr int nA = BM / 8 / W;                  // 1 KB copies of eight activation rows per stage
   static constexpr int MI = BM / 32;                     // 32-row MFMA blocks per wave
   // activation copies per wave when only the first `live` 32-row blocks hold rows
   static constexpr int nA_live(int live) { return (4 * live + W - 1) / W < nA ? (4 * live + W - 1) / W : nA; }
-  static constexpr int copies(int live) { return nA_live(live) + nB + nS; }
-  // workgroups per CU that the three stage buffers allow (at most two), and
-  // the waves per SIMD that gives
-  static constexpr int kPerCU = 3 * kBytes * 2 <= 160 * 1024 ? 2 : 1;
+  // workgroups per CU that the activation ring allows (at most two), and the
+  // waves per SIMD that gives
+  static constexpr int kPerCU = 2 * kRingBytes <= 160 * 1024 ? 2 : 1;
   static constexpr int kWavesPerSimd = kPerCU * W / 4;
-  static_assert(nA * 8 * W == BM && nB * 2 * W == kBlocks, "copies split evenly over the waves");
+  static_assert(nA * 8 * W == BM, "copies split evenly over the waves");
 };
 
 // A value every lane holds alike, moved to a scalar register.
@@ -106,143 +104,10 @@ __device__ __forceinline__ int swz(int c, int r) { return c ^ (r & 7) ^ ((r >> 3
 // the compiler placed after the barrier still reads its result.
 #define MOE_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | ((((n) >> 4) & 3) << 14))
 
-// Per-lane global source pointers of one wave's copies: activation rows,
-// code half-tiles, scale dwords.  Advance by stage: activations +128 B, codes
-// +512 B, scales per 128-K block (see scale_off).
-template <class C>
-struct StageSrc {
-  const uint8_t* a[C::nA];
-  const uint8_t* b[C::nB];
-  const uint8_t* s[C::nS];
-};
-
+// Byte offset of stage st's scale dwords in a row block's scale groups: one
+// group per four 128-K blocks, a dword per chunk lane of the half tile.
 __device__ __forceinline__ size_t scale_off(int st) {
   return (size_t)(st >> 3) * kScaleGroupBytes + (size_t)(st & 1) * 128;   // group of 4 blocks, half of the lanes
-}
-
-// Copy number c (0 .. copies(LIVE)-1) of this wave's share of stage st.
-template <class C, int LIVE>
-__device__ __forceinline__ void issue_copy(uint8_t* buf, const StageSrc<C>& src, int st, int wave, int c) {
-  constexpr int W = C::W;
-  constexpr int NA = C::nA_live(LIVE);
-  if (c < NA) {                      // rows 8i..8i+7 of the stage, i = wave + W j
-    const int j = c;
-    __builtin_amdgcn_global_load_lds((glob_void_t*)(src.a[j] + (size_t)st * (kStageK * 2)),
-                                     (lds_void_t*)(buf + (wave + W * j) * 1024), 16, 0, 0);
-  } else if (c < NA + C::nB) {        // code half-tiles of row blocks 2i, 2i+1
-    const int j = c - NA;
-    __builtin_amdgcn_global_load_lds((glob_void_t*)(src.b[j] + (size_t)st * kHalfTile),
-                                     (lds_void_t*)(buf + C::kA + (wave + W * j) * 1024), 16, 0, 0);
-  } else {                            // their scale dwords
-    const int j = c - NA - C::nB;
-    __builtin_amdgcn_global_load_lds((glob_void_t*)(src.s[j] + scale_off(st)),
-                                     (lds_void_t*)(buf + C::kA + C::kB + (wave + W * j) * 256), 4, 0, 0);
-  }
-}
-
-template <class C, int LIVE>
-__device__ __forceinline__ void issue_stage(uint8_t* buf, const StageSrc<C>& src, int st, int wave) {
-#pragma unroll
-  for (int c = 0; c < C::copies(LIVE); ++c) issue_copy<C, LIVE>(buf, src, st, wave, c);
-}
-
-// The K loop of one wave over its MI 32-row blocks, of which LIVE hold rows
-// (blocks past them are padding: their activations are neither copied nor
-// multiplied).  `wn` is the wave's 64-column group.
-template <class C, int LIVE>
-__device__ __forceinline__ void k_loop(uint8_t* smem, const StageSrc<C>& src, int S, int wave, int lane,
-                                       f32x16_t (&acc)[C::MI][2]) {
-  constexpr int NJ = 2;
-  constexpr int LOADS = C::copies(LIVE);
-  const int wn = wave;
-  const int n32 = lane & 31, h = lane >> 5;
-  uint8_t* cur = smem;
-  uint8_t* nxt = smem + C::kBytes;
-  uint8_t* nxt2 = smem + 2 * C::kBytes;
-  issue_stage<C, LIVE>(cur, src, 0, wave);
-  if (S > 1) issue_stage<C, LIVE>(nxt, src, 1, wave);
-  // this lane's reads inside a stage
-  const int lp = (n32 & 15) + 16 * h;
-  const int boff = (wn * (2 * NJ) + (n32 >> 4)) * kHalfTile + lp * 16;  // + 2*nj*kHalfTile
-  const int soff = C::kA + C::kB + ((wn * (2 * NJ) + (n32 >> 4)) * 32 + lp) * 4;
-  const int aoff = n32 * (kStageK * 2);
-  for (int st = 0; st < S; ++st) {
-    if (st + 1 < S) MOE_WAIT_VMCNT(LOADS);   // this wave's loads of stage st have landed
-    else MOE_WAIT_VMCNT(0);
-    // ... and every wave's; stage st-1 is fully consumed.  A bare s_barrier: the
-    // fence of __syncthreads would also drain the stages still in flight.  The
-    // empty asm statements keep the compiler from moving LDS accesses across it.
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    // stage st+2's copies go out a quarter per k-step, between the MFMA
-    // batches: issued all at once after the barrier, every wave's copies queue
-    // on the CU's texture path together and hold back its first MFMAs
-    const bool refill = st + 2 < S;
-    const int sh = ((st >> 1) & 3) * 8;
-    u32x4_t bc[NJ];
-    uint32_t sraw[NJ];
-#pragma unroll
-    for (int nj = 0; nj < NJ; ++nj) {
-      sraw[nj] = *reinterpret_cast<const uint32_t*>(cur + soff + 2 * nj * 32 * 4);
-      bc[nj] = *reinterpret_cast<const u32x4_t*>(cur + C::kA + boff + 2 * nj * kHalfTile);
-    }
-    // Step s+1's activation fragments are read while step s multiplies.  Per
-    // step: the dequantised weights and the first MFMA (the compiler waits
-    // there for this step's fragments, read a step earlier), then this step's
-    // share of the copies, in a block of its own, then the next step's reads
-    // and the other MFMAs.  A copy issued while an LDS read is outstanding
-    // makes the compiler wait with lgkmcnt(0) at that read's first use -- with
-    // the next step's reads already issued, that wait would cover them too.
-    const uint8_t* arow = cur + aoff;
-    bf16x8_t Ac[LIVE], An[LIVE];
-#pragma unroll
-    for (int mi = 0; mi < LIVE; ++mi)
-      Ac[mi] = *reinterpret_cast<const bf16x8_t*>(arow + mi * 32 * (kStageK * 2) + swz(4 * h, n32) * 16);
-    // every read of the stage head is issued before the first of them is used
-    // (left to itself the compiler waits for the scale bytes before issuing
-    // the other reads: two LDS round trips at every stage head)
-    __builtin_amdgcn_sched_barrier(0);
-    float bs[NJ];
-#pragma unroll
-    for (int nj = 0; nj < NJ; ++nj) bs[nj] = e8m0_to_f32((sraw[nj] >> sh) & 0xFFu);
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      bf16x8_t B[NJ];
-#pragma unroll
-      for (int nj = 0; nj < NJ; ++nj) B[nj] = dequant8(bc[nj][s], bs[nj]);
-      acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Ac[0], B[0], acc[0][0], 0, 0, 0);
-      if (refill) {
-#pragma unroll
-        for (int c = s * LOADS / 4; c < (s + 1) * LOADS / 4; ++c)
-          issue_copy<C, LIVE>(nxt2, src, st + 2, wave, c);
-      }
-      if (s < 3) {
-#pragma unroll
-        for (int mi = 0; mi < LIVE; ++mi)
-          An[mi] =
-              *reinterpret_cast<const bf16x8_t*>(arow + mi * 32 * (kStageK * 2) + swz(4 * h + s + 1, n32) * 16);
-      }
-#pragma unroll
-      for (int mi = 0; mi < LIVE; ++mi)
-#pragma unroll
-        for (int nj = 0; nj < NJ; ++nj)
-          if (mi + nj > 0)
-            acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Ac[mi], B[nj], acc[mi][nj], 0, 0, 0);
-      // the reads first (left to itself the compiler puts them behind the MFMAs)
-      if (s < 3) __builtin_amdgcn_sched_group_barrier(0x100, LIVE, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, NJ * LIVE - 1, 0);
-      __builtin_amdgcn_sched_barrier(0);
-      if (s < 3) {
-#pragma unroll
-        for (int mi = 0; mi < LIVE; ++mi) Ac[mi] = An[mi];
-      }
-    }
-    uint8_t* t = cur;
-    cur = nxt;
-    nxt = nxt2;
-    nxt2 = t;
-  }
 }
 
 // Stages ring_pass runs: s0 + P .. s0 + N - 1 that lie below s0 + n, ring slots P .. N - 1.
@@ -277,7 +142,8 @@ __device__ __forceinline__ void k_loop_r(uint8_t* smem, const uint8_t* const (&s
   constexpr int G = NA + 2 * NJ;         // loads per wave and stage
   constexpr int R = D + 1;               // ring slots
   constexpr uint32_t kPastEnd = 0x80000000u;
-  static_assert(R * C::kA * C::kPerCU <= 160 * 1024, "activation ring");
+  constexpr int kSlot = NA * W * 1024;   // the stage's live activation rows
+  static_assert(R * kSlot <= kRingBytes && (D - 1) * G <= 63, "activation ring, vmcnt range");
   const int n32 = lane & 31, h = lane >> 5;
   const int aoff = n32 * (kStageK * 2);
   u32x4_t bc[R][NJ];
@@ -288,7 +154,7 @@ __device__ __forceinline__ void k_loop_r(uint8_t* smem, const uint8_t* const (&s
     constexpr int slot = decltype(slot_c)::value;
     const bool real = st < S;
     const int sa = min(st, S - 1);
-    uint8_t* buf = smem + slot * C::kA;
+    uint8_t* buf = smem + slot * kSlot;
 #pragma unroll
     for (int c = 0; c < G; ++c) {
       if (c < first || c >= last) continue;
@@ -317,7 +183,7 @@ __device__ __forceinline__ void k_loop_r(uint8_t* smem, const uint8_t* const (&s
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    const uint8_t* arow = smem + p * C::kA + aoff;
+    const uint8_t* arow = smem + p * kSlot + aoff;
     const int sh = ((st >> 1) & 3) * 8;
     bf16x8_t Ac[LIVE], An[LIVE];
 #pragma unroll
@@ -394,7 +260,7 @@ __global__ __launch_bounds__(W * kWave)
 __attribute__((amdgpu_waves_per_eu(Cfg<BM, W>::kWavesPerSimd, Cfg<BM, W>::kWavesPerSimd)))
 void fc_pre(FcArgs a, int slices) {
   using C = Cfg<BM, W>;
-  __shared__ __align__(1024) uint8_t smem[(kDepth + 1) * C::kA];
+  __shared__ __align__(1024) uint8_t smem[kRingBytes];
   __shared__ int s_item;
 
   const int ntiles = *a.tile_count;
@@ -511,10 +377,10 @@ __device__ __noinline__ void fc_pre_item(const FcArgs& a, uint8_t* smem, int sli
   const int S = 2 * M.kb;    // stages
   static_assert(MI == 4, "128-row tiles");
   switch (live) {
-    case 1: k_loop_r<C, 1, kDepth>(smem, srcA, rcode, rscale, coff, soff, S, wave, lane, acc); break;
-    case 2: k_loop_r<C, 2, kDepth>(smem, srcA, rcode, rscale, coff, soff, S, wave, lane, acc); break;
-    case 3: k_loop_r<C, 3, kDepth>(smem, srcA, rcode, rscale, coff, soff, S, wave, lane, acc); break;
-    default: k_loop_r<C, 4, kDepth>(smem, srcA, rcode, rscale, coff, soff, S, wave, lane, acc); break;
+    case 1: k_loop_r<C, 1, depth_for<1>()>(smem, srcA, rcode, rscale, coff, soff, S, wave, lane, acc); break;
+    case 2: k_loop_r<C, 2, depth_for<2>()>(smem, srcA, rcode, rscale, coff, soff, S, wave, lane, acc); break;
+    case 3: k_loop_r<C, 3, depth_for<3>()>(smem, srcA, rcode, rscale, coff, soff, S, wave, lane, acc); break;
+    default: k_loop_r<C, 4, depth_for<4>()>(smem, srcA, rcode, rscale, coff, soff, S, wave, lane, acc); break;
   }
   const int next = threadIdx.x == 0 ? atomicAdd(counter, 1) : 0;
   const int n32 = lane & 31, h = lane >> 5;
