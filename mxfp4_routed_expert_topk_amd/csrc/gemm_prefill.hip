@@ -183,6 +183,9 @@ __device__ __forceinline__ void k_loop_r(uint8_t* smem, const uint8_t* const (&s
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
+    // raised issue priority while the wave multiplies (measured 1-2 % faster
+    // on the 4096-token Zipf and 1536-token layers)
+    __builtin_amdgcn_s_setprio(1);
     const uint8_t* arow = smem + p * kSlot + aoff;
     const int sh = ((st >> 1) & 3) * 8;
     bf16x8_t Ac[LIVE], An[LIVE];
@@ -221,6 +224,7 @@ __device__ __forceinline__ void k_loop_r(uint8_t* smem, const uint8_t* const (&s
         for (int mi = 0; mi < LIVE; ++mi) Ac[mi] = An[mi];
       }
     }
+    __builtin_amdgcn_s_setprio(0);
   };
 
   // one group after another: the waits count whole groups in issue order

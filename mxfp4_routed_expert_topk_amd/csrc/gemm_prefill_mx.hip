@@ -51,8 +51,12 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 
 constexpr int kRows = kPrefillMxRows;       // rows per tile
 constexpr int kNBW = 4;                     // row blocks (16 output columns each) per wave
-constexpr int kDepth = 2;                   // stages loaded ahead of the one multiplied
-constexpr int kBufs = kDepth + 1;           // LDS stage buffers
+// Stages loaded ahead of the one multiplied: three for tiles of at most 96
+// rows, whose accumulators leave room for a fourth ring slot, else two.
+template <int LIVE>
+constexpr int depth_for() { return LIVE <= 3 ? 3 : 2; }
+constexpr int kMaxDepth = 3;
+constexpr int kBufs = kMaxDepth + 1;        // LDS stage buffers
 constexpr int kStageA = kRows * kTileK;       // 128 rows x 128 E4M3
 constexpr int kStageBytes = kStageA + kRows * 4;   // + each row's four E8M0 bytes of the stage
 
@@ -61,34 +65,7 @@ constexpr int kStageBytes = kStageA + kRows * 4;   // + each row's four E8M0 byt
 
 __device__ __forceinline__ int swz(int c, int r) { return c ^ (r & 7) ^ ((r >> 3) & 1); }
 
-// Wait until at most `ahead` stage groups of this wave's loads are still
-// outstanding; a group is NA + B loads (s_waitcnt takes an immediate, hence
-// the cases over the wave-uniform `ahead`).
-template <int B, int NA>
-__device__ __forceinline__ void wait_ahead(int ahead) {
-  switch (ahead) {
-    case 0: MOE_WAIT_VM_LGKM(0); break;
-    case 1: MOE_WAIT_VM_LGKM(1 * (NA + B)); break;
-    case 2: MOE_WAIT_VM_LGKM(2 * (NA + B)); break;
-    case 3: MOE_WAIT_VM_LGKM(3 * (NA + B)); break;
-    case 4: MOE_WAIT_VM_LGKM(4 * (NA + B)); break;
-    case 5: MOE_WAIT_VM_LGKM(5 * (NA + B)); break;
-    case 6: MOE_WAIT_VM_LGKM(6 * (NA + B)); break;
-    default: MOE_WAIT_VM_LGKM(7 * (NA + B)); break;
-  }
-}
-template <int B>
-__device__ __forceinline__ void wait_groups(int ahead, int na) {
-  switch (na) {
-    case 0: wait_ahead<B, 0>(ahead); break;
-    case 1: wait_ahead<B, 1>(ahead); break;
-    case 2: wait_ahead<B, 2>(ahead); break;
-    case 3: wait_ahead<B, 3>(ahead); break;
-    default: wait_ahead<B, 4>(ahead); break;
-  }
-}
-static_assert(kDepth >= 1 && kDepth <= 8, "wait_ahead covers up to seven stage groups behind the current one");
-static_assert((kDepth - 1) * (16 / 4 + 1 + 2 * kNBW) <= 63, "vmcnt holds at most 63");
+static_assert((kMaxDepth - 1) * (16 / 4 + 1 + 2 * kNBW) <= 63, "vmcnt holds at most 63");
 
 // Stages s0 + P .. s0 + N - 1 that lie below s0 + n, ring slots P .. N - 1.
 template <int P, int N, class F>
@@ -103,7 +80,7 @@ __device__ __forceinline__ void ring_pass(F& f, int s0, int n) {
 
 // WV waves per workgroup: 8 (one workgroup per CU, 512 columns) or 4 (two per
 // CU, 256 columns).
-template <bool FC1, int LIVE, int WV>
+template <bool FC1, int LIVE, int WV, int kDepth = depth_for<LIVE>()>
 __device__ __forceinline__ void tile_body(const FcArgs& a, uint8_t* sa, int e, int row0, int rows, int slice) {
   static_assert(WV == 4 || WV == 8, "four or eight waves per workgroup");
   constexpr int kWaves = WV;
@@ -125,11 +102,15 @@ __device__ __forceinline__ void tile_body(const FcArgs& a, uint8_t* sa, int e, i
   const __amdgpu_buffer_rsrc_t rascl = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(a.a_scales), (short)0, a.a_rows * sgroups, kRsrcWord3);
   // activation copies: group g (rows 8g .. 8g+7) is copied by wave g % kWaves;
-  // lane L fills row 8g + L/8 at chunk position L%8
-  const int na = (GROUPS - wave + kWaves - 1) / kWaves;   // this wave's groups: 0 .. kCopySlots
-  uint32_t aoff[kCopySlots];
+  // lane L fills row 8g + L/8 at chunk position L%8.  Every wave issues NA
+  // copies per stage: a wave with fewer live groups than that fills rows past
+  // the live ones (read by no MFMA) with an out-of-range zero copy, so that
+  // every wave issues the same count and the waits below are constants.
+  constexpr int NA = (GROUPS + kWaves - 1) / kWaves;
+  static_assert(NA <= kCopySlots, "copy slots");
+  uint32_t aoff[NA];
 #pragma unroll
-  for (int j = 0; j < kCopySlots; ++j) {
+  for (int j = 0; j < NA; ++j) {
     const int r = 8 * (wave + kWaves * j) + (lane >> 3);
     const int rr = min(r, rows - 1);
     const int ar = FC1 ? a.perm[row0 + rr] / a.top_k : row0 + rr;
@@ -177,10 +158,11 @@ __device__ __forceinline__ void tile_body(const FcArgs& a, uint8_t* sa, int e, i
     uint8_t* buf = sa + bi * kStageBytes;
     const bool real = s < S;
 #pragma unroll
-    for (int j = 0; j < kCopySlots; ++j)
-      if (kWaves == 4 ? j < LIVE : j < na)   // four waves: every wave copies LIVE groups, a constant
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(racts, (lds_void_t*)(buf + (wave + kWaves * j) * 1024), 16,
-                                                 real ? aoff[j] : kPastEnd, real ? s * kTileK : 0, 0, 0);
+    for (int j = 0; j < NA; ++j) {
+      const bool live = real && wave + kWaves * j < GROUPS;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(racts, (lds_void_t*)(buf + (wave + kWaves * j) * 1024), 16,
+                                               live ? aoff[j] : kPastEnd, live ? s * kTileK : 0, 0, 0);
+    }
     if (lane < kScaleLanes)   // part of the wave: one operation all the same
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rascl, (lds_void_t*)(buf + kStageA + kScaleLanes * 4 * wave), 4,
                                                real ? soff : kPastEnd, real ? 4 * s : 0, 0, 0);
@@ -191,10 +173,16 @@ __device__ __forceinline__ void tile_body(const FcArgs& a, uint8_t* sa, int e, i
     for (int j = 0; j < kNBW; ++j)
       q[j] = __builtin_amdgcn_raw_buffer_load_b128(rcode, real ? lane * 16 : kPastEnd,
                                                    real ? j * bstride + s * kTileBytes : 0, 0);
+    // the dword of the lane's four E8M0 bytes in the stage's scale group (its
+    // byte s % 4 is taken at the MFMA): loaded as a byte, the value would be
+    // zero-extended by a copy that waits for the load right after it is issued.
+    // Past the end: the last stage's dword again (an out-of-range offset here
+    // makes the compiler branch around the loads, and its waits then count
+    // the loads of later stages too).
+    const int sg = (min(s, S - 1) >> 2) * kScaleGroupBytes;
 #pragma unroll
     for (int j = 0; j < kNBW; ++j)
-      sb[j] = __builtin_amdgcn_raw_buffer_load_b8(
-          rscale, real ? lane * 4 : kPastEnd, real ? j * sstride + (s >> 2) * kScaleGroupBytes + (s & 3) : 0, 0);
+      sb[j] = __builtin_amdgcn_raw_buffer_load_b32(rscale, lane * 4, j * sstride + sg, 0);
   };
 
   // A operand position of this lane inside a staged 16-row block
@@ -213,14 +201,14 @@ __device__ __forceinline__ void tile_body(const FcArgs& a, uint8_t* sa, int e, i
     // this wave's loads of stage st have landed (the kDepth - 1 groups after
     // it may still be in flight) and its LDS reads of stage st-1 have
     // returned; the barrier extends both to every wave
-    if constexpr (kWaves == 4) MOE_WAIT_VM_LGKM((kDepth - 1) * (LIVE + 1 + 2 * kNBW));   // na == LIVE
-    else wait_groups<1 + 2 * kNBW>(kDepth - 1, na);
+    MOE_WAIT_VM_LGKM((kDepth - 1) * (NA + 1 + 2 * kNBW));
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    issue_lds((st + kDepth) % kBufs, st + kDepth);   // into the buffer of stage st-1
+    issue_lds((st + kDepth) % kRing, st + kDepth);   // into the buffer of stage st-1
     load_regs(bq[(p + kDepth) % kRing], bs[(p + kDepth) % kRing], st + kDepth);
-    const uint8_t* cur = sa + (st % kBufs) * kStageBytes;
+    const uint8_t* cur = sa + (st % kRing) * kStageBytes;
+    const int sh = 8 * (st & 3);
     const uint8_t* curs = cur + kStageA;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
@@ -233,7 +221,7 @@ __device__ __forceinline__ void tile_body(const FcArgs& a, uint8_t* sa, int e, i
       for (int j = 0; j < kNBW; ++j) {
         const i32x8_t Bf = {(int)bq[p][j][0], (int)bq[p][j][1], (int)bq[p][j][2], (int)bq[p][j][3], 0, 0, 0, 0};
         acc[mb][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(Af, Bf, acc[mb][j], 0, 4, 0, sc, 0,
-                                                                      (int)bs[p][j]);
+                                                                      (int)((bs[p][j] >> sh) & 0xFFu));
       }
     }
     // The stage's MFMAs stay above the next barrier (this empty statement
@@ -246,10 +234,12 @@ __device__ __forceinline__ void tile_body(const FcArgs& a, uint8_t* sa, int e, i
       for (int j = 0; j < kNBW; ++j) asm volatile("" ::"v"(acc[mb][j]));
   };
 
+  // one group after another: the waits count whole groups in issue order
 #pragma unroll
   for (int d = 0; d < kDepth; ++d) {
     issue_lds(d, d);
     load_regs(bq[d], bs[d], d);
+    __builtin_amdgcn_sched_barrier(0);
   }
   int s0 = 0;
   for (; s0 + kRing <= S; s0 += kRing) ring_pass<0, kRing>(run_stage, s0, kRing);
