@@ -36,10 +36,10 @@ Prints ONE JSON line:
 from __future__ import annotations
 
 import argparse
+import glob
 import hashlib
 import json
 import os
-import subprocess
 import sys
 import time
 
@@ -78,21 +78,32 @@ def pct(a, q):
 
 # ----------------------------------------------------------------------------- box state and ceilings
 def gpu_state():
-    """Clock levels, power and performance level of the GPU(s) as rocm-smi
-    reports them (the pages saw a clock policy move their numbers)."""
+    """Clock levels, power and performance level of the GPU(s), read from the
+    amdgpu sysfs files (the pages saw a clock policy move their numbers).  No
+    helper program is started: this process has initialised the GPU by then."""
     out = {}
     try:
-        r = subprocess.run(["rocm-smi", "--showclocks", "--showpower", "--showperflevel", "--json"],
-                           capture_output=True, text=True, timeout=20)
-        data = json.loads(r.stdout) if r.stdout.strip().startswith("{") else {}
-        for card, v in data.items():
-            if not isinstance(v, dict):
+        for dev in sorted(glob.glob("/sys/class/drm/card*/device")):
+            if not os.path.exists(os.path.join(dev, "pp_dpm_sclk")):
                 continue
-            keep = {k: v[k] for k in v if any(s in k.lower() for s in ("sclk", "mclk", "fclk", "power", "perf"))}
-            if keep:
-                out[card] = keep
-        if not out:
-            out["rocm_smi"] = (r.stdout or r.stderr).strip()[:400]
+            rec = {}
+            for f in ("pp_dpm_sclk", "pp_dpm_mclk", "pp_dpm_fclk"):
+                try:
+                    cur = [ln.strip() for ln in open(os.path.join(dev, f)) if ln.strip().endswith("*")]
+                    rec[f[7:]] = cur[0] if cur else None
+                except OSError:
+                    pass
+            try:
+                rec["perf_level"] = open(os.path.join(dev, "power_dpm_force_performance_level")).read().strip()
+            except OSError:
+                pass
+            for pw in glob.glob(os.path.join(dev, "hwmon", "hwmon*", "power1_*")):
+                if pw.endswith(("_average", "_input")):
+                    try:
+                        rec["power_w"] = round(int(open(pw).read()) / 1e6, 1)
+                    except (OSError, ValueError):
+                        pass
+            out[os.path.basename(os.path.dirname(dev))] = rec
     except Exception as e:          # the state is a record, never a reason to fail the run
         out["error"] = repr(e)[:200]
     return out
