@@ -398,16 +398,16 @@ def counter_traffic(workload, tag):
 
 
 def cpu_baseline():
-    """The fp64 oracle, as it stands, on 24 tokens of the decode M=128 batch,
-    its experts evaluated on a thread per host core (BLAS single-threaded
-    inside each)."""
+    """The fp64 oracle, as it stands, on the whole decode M=128 batch (about
+    10 s of host work), its experts evaluated on a thread per host core (BLAS
+    single-threaded inside each)."""
     from concurrent.futures import ThreadPoolExecutor
     from threadpoolctl import threadpool_limits
     import oracle
     import workloads as W
     threads = max(1, min(16, os.cpu_count() or 1))
     case = W.config_case(1, m=128)
-    toks = list(range(24))
+    toks = list(range(case.shape.tokens))
     cache = {e: case.expert(e) for e in np.unique(case.topk_ids[toks]) if 0 <= e < case.shape.experts}
     with ThreadPoolExecutor(threads) as ex, threadpool_limits(1, "blas"):
         t0 = time.perf_counter()
@@ -415,7 +415,7 @@ def cpu_baseline():
                        tokens=toks, pool=ex)
         dt = time.perf_counter() - t0
     return {"value": round(len(toks) / dt, 4), "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"fp64 numpy oracle over tokens 0..{len(toks) - 1} of the decode M=128 batch ({len(cache)} experts, "
+            "sample": f"fp64 numpy oracle over all {len(toks)} tokens of the decode M=128 batch ({len(cache)} experts, "
                       f"weight generation excluded): {dt:.1f}s on {threads} threads (one expert each at a time, "
                       f"BLAS single-threaded); the host reports {os.cpu_count()} CPUs"}
 
