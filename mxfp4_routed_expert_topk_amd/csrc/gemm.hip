@@ -107,7 +107,7 @@ hipError_t launch_dec(const FcArgs& a, int tiles_max, hipStream_t stream) {
 
 // The K split is fixed per matrix (it sets the fp32 summation order); the
 // row-block group width and the load depth only change the schedule.
-constexpr int kSmallTokens = 16;
+constexpr int kSmallTokens = 4;
 
 template <bool FC1, bool MX, int NBW, int P, bool PER_ROUTE = false>
 hipError_t launch_sched(const FcArgs& a, int tiles_max, hipStream_t stream) {
@@ -116,8 +116,10 @@ hipError_t launch_sched(const FcArgs& a, int tiles_max, hipStream_t stream) {
 }
 
 // Schedules (every row-block count here is a multiple of 8: H, I multiples of
-// 128).  Up to 16 tokens: two row blocks per workgroup, two column blocks
-// loaded ahead; larger batches: four (FC1) or eight (FC2) row blocks.
+// 128).  Up to 4 tokens: two row blocks per workgroup, two column blocks
+// loaded ahead; larger batches: four (FC1) or eight (FC2) row blocks (measured
+// 9-10 % faster than two from 8 to 16 tokens; eight FC1 row blocks, or three
+// column blocks ahead, were slower there).
 template <bool FC1, bool MX>
 hipError_t launch_fc(const FcArgs& a, int tiles_max, int tokens, hipStream_t stream) {
   if (tokens <= kSmallTokens) return launch_sched<FC1, MX, 2, 2>(a, tiles_max, stream);

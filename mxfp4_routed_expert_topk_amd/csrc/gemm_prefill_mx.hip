@@ -56,6 +56,9 @@ constexpr int kNBW = 4;                     // row blocks (16 output columns eac
 template <int LIVE>
 constexpr int depth_for() { return LIVE <= 3 ? 3 : 2; }
 constexpr int kMaxDepth = 3;
+// Cache policy of FC2's weight loads: non-temporal (measured 3 % faster in FC2;
+// the same policy made FC1 6 % slower).
+constexpr int kNonTemporal = 2;
 constexpr int kBufs = kMaxDepth + 1;        // LDS stage buffers
 constexpr int kStageA = kRows * kTileK;       // 128 rows x 128 E4M3
 constexpr int kStageBytes = kStageA + kRows * 4;   // + each row's four E8M0 bytes of the stage
@@ -172,7 +175,7 @@ __device__ __forceinline__ void tile_body(const FcArgs& a, uint8_t* sa, int e, i
 #pragma unroll
     for (int j = 0; j < kNBW; ++j)
       q[j] = __builtin_amdgcn_raw_buffer_load_b128(rcode, real ? lane * 16 : kPastEnd,
-                                                   real ? j * bstride + s * kTileBytes : 0, 0);
+                                                   real ? j * bstride + s * kTileBytes : 0, FC1 ? 0 : kNonTemporal);
     // the dword of the lane's four E8M0 bytes in the stage's scale group (its
     // byte s % 4 is taken at the MFMA): loaded as a byte, the value would be
     // zero-extended by a copy that waits for the load right after it is issued.
