@@ -117,13 +117,13 @@ hipError_t launch_sched(const FcArgs& a, int tiles_max, hipStream_t stream) {
 
 // Schedules (every row-block count here is a multiple of 8: H, I multiples of
 // 128).  Up to 4 tokens: two row blocks per workgroup, two column blocks
-// loaded ahead; larger batches: four (FC1) or eight (FC2) row blocks (measured
-// 9-10 % faster than two from 8 to 16 tokens; eight FC1 row blocks, or three
-// column blocks ahead, were slower there).
+// loaded ahead; larger batches: four row blocks (measured 9-10 % faster than
+// two from 8 to 16 tokens; eight FC1 row blocks, or three column blocks ahead,
+// were slower there), eight for FC2 above 16 tokens.
 template <bool FC1, bool MX>
 hipError_t launch_fc(const FcArgs& a, int tiles_max, int tokens, hipStream_t stream) {
   if (tokens <= kSmallTokens) return launch_sched<FC1, MX, 2, 2>(a, tiles_max, stream);
-  if (FC1) return launch_sched<FC1, MX, 4, 2>(a, tiles_max, stream);
+  if (FC1 || tokens <= 16) return launch_sched<FC1, MX, 4, 2>(a, tiles_max, stream);
   return launch_sched<FC1, MX, 8, 2>(a, tiles_max, stream);
 }
 
