@@ -1,24 +1,25 @@
 // Grouped FC1 / FC2 for large batches (prefill): MFMA-bound tiles.
 //
 // Work item = (BM-row tile of one expert's rows, 256-column slice of the
-// weight rows).  A workgroup of four waves runs a three-stage LDS pipeline
-// over 64-K stages: each stage holds the BM gathered activation rows (bf16),
-// the sixteen half-tiles of raw repacked E2M1 codes of the slice and their
-// E8M0 bytes, written straight from global memory by global_load_lds_dwordx4
-// (no staging registers).  Each wave owns all BM rows x one 64-column quarter
-// on v_mfma_f32_32x32x16_bf16 and dequantises its weight fragments in
-// registers with the gfx950 scaled converter (value * 2^(scale-127), exact in
-// bf16): every converted fragment feeds BM/32 MFMAs, and a code byte crosses
-// LDS once instead of as two bf16 bytes per weight.  32-row blocks that lie
-// wholly past the tile's rows (Zipf-routed experts leave many) issue no MFMA
-// and their activation rows are not copied.
+// weight rows).  A workgroup of four waves runs over 64-K stages.  Each wave
+// owns all BM rows x one 64-column quarter on v_mfma_f32_32x32x16_bf16: its
+// weight chunks (the 16 code bytes a lane multiplies in each of its two
+// 32-column blocks, and the dwords holding their E8M0 bytes) come straight
+// from global memory into a per-wave register ring, several stages ahead, and
+// are dequantised in registers with the gfx950 scaled converter (value *
+// 2^(scale-127), exact in bf16), every converted fragment feeding BM/32
+// MFMAs.  The activation rows, which the four waves share, pass through a
+// ring of LDS stages written by global_load_lds_dwordx4 (no staging
+// registers).  32-row blocks that lie wholly past the tile's rows (Zipf-routed
+// experts leave many) issue no MFMA and their activation rows are not copied;
+// tiles with fewer live rows keep more stages in flight.
 //
 // Step order inside a stage: the first MFMA of a step (its operands were read
-// a step earlier), then the step's share of the next copies, then the next
-// step's LDS reads, then the other MFMAs.  The compiler stops counting LDS
-// reads precisely once an LDS-DMA copy is issued behind them and waits for
-// lgkmcnt(0) at their first use; in this order that wait only ever covers
-// reads that are a full step old.
+// a step earlier), then the step's share of the next stage's loads, then the
+// next step's LDS reads, then the other MFMAs.  The compiler stops counting
+// LDS reads precisely once an LDS-DMA copy is issued behind them and waits
+// for lgkmcnt(0) at their first use; in this order that wait only ever
+// covers reads that are a full step old.
 //
 // MFMA K order: in the stage covering K [64q, 64q+64) of a 128-K column block
 // (q = 0, 1), step s (16 K) of lane l (column n = l%32, half h = l/32)
