@@ -108,6 +108,11 @@ moe_status moe_mxfp4_plan(const moe_mxfp4_config* cfg, const uint8_t* w13_codes,
  *                 on entry do not matter (the call sets every word it reads,
  *                 including the work counters of the large-batch kernels,
  *                 which its first kernel zeroes on the stream)
+ * Intermediate precision: g and u are fp32 sums; h is rounded to bf16 (bf16
+ * activations) or requantised to MXFP8 before FC2; batches that take the
+ * 128-row-tile kernels (T*k >= 16*E) also round each route's y to bf16 before
+ * the fp32 slot-order sum (b12x PR #339: the fused-sum epilogue reduces bf16
+ * routed outputs).
  * Enqueue-only: no host synchronisation and no allocation, so the call can be
  * captured in a HIP graph.  Inputs and the repacked weights are never written.
  * Concurrent calls sharing one workspace race. */

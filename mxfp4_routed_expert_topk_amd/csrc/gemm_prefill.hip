@@ -88,7 +88,7 @@ struct Cfg {
   static_assert(nA * 8 * W == BM, "copies split evenly over the waves");
   // a wave's share of the ring when it stages its outputs
   static constexpr int kStageOut = kRingBytes / W;
-  static_assert(BM * 64 <= kStageOut && kStageOut % (32 * 256) == 0, "output staging fits the ring");
+  static_assert(BM * 64 <= kStageOut && kStageOut % (32 * 128) == 0, "output staging fits the ring");
 };
 
 // A value every lane holds alike, moved to a scalar register.
@@ -434,8 +434,9 @@ __device__ __noinline__ void fc_pre_item(const FcArgs& a, uint8_t* smem, int sli
       if (rr < rows) store16(static_cast<uint16_t*>(out) + (size_t)(row0 + rr) * ldo + hc0 + c4 * 8, v);
     }
   } else {
-    // fp32 y, RB rows at a time: row-major [RB][64] fp32
-    constexpr int RB = C::kStageOut / 256, MG = RB / 32;       // rows and 32-row blocks per pass
+    // y rounded to bf16 (the routes' outputs are summed in fp32 by the
+    // combine), RB rows at a time: row-major [RB][64] bf16
+    constexpr int RB0 = C::kStageOut / 128, RB = RB0 < BM ? RB0 : BM, MG = RB / 32;
     const int c0 = (nb0 + wave * (2 * NJ)) * kTileN;           // the wave's first output column
 #pragma unroll
     for (int g = 0; g < MI / MG; ++g) {
@@ -449,16 +450,16 @@ __device__ __noinline__ void fc_pre_item(const FcArgs& a, uint8_t* smem, int sli
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int r = m2 * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
-            *reinterpret_cast<float*>(stg + r * 256 + (nj * 32 + n32) * 4) = acc[mi][nj][i];
+            *reinterpret_cast<uint16_t*>(stg + r * 128 + (nj * 32 + n32) * 2) = f32_to_bf16_rne(acc[mi][nj][i]);
           }
       }
       asm volatile("" ::: "memory");
       const int nrows = min(RB, live * 32 - g * RB);
-      for (int k = 0; k < nrows / 4; ++k) {                     // 4 rows of 256 B per pass
-        const int rr = k * 4 + (lane >> 4), ch = lane & 15;
-        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stg + rr * 256 + ch * 16);
+      for (int k = 0; k < nrows / 8; ++k) {                     // 8 rows of 128 B per pass
+        const int rr = k * 8 + (lane >> 3), ch = lane & 7;
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stg + rr * 128 + ch * 16);
         const int gr = g * RB + rr;
-        if (gr < rows) store16(static_cast<float*>(out) + (size_t)(row0 + gr) * ldo + c0 + ch * 4, v);
+        if (gr < rows) store16(static_cast<uint16_t*>(out) + (size_t)(row0 + gr) * ldo + c0 + ch * 8, v);
       }
       asm volatile("" ::: "memory");
     }

@@ -38,7 +38,8 @@
 //
 // FC1: row blocks come in (gate j, up j) pairs (interleaved repack); the
 // epilogue requantises h = silu(g) * u to MXFP8 (E4M3 codes, one E8M0 per 32
-// columns), which FC2 reads.  FC2: fp32 y rows in route-row order.
+// columns), which FC2 reads.  FC2: y rows in route-row order, rounded to bf16
+// (the combine sums them in fp32).
 #include <type_traits>
 
 #include "moe_internal.h"
@@ -288,11 +289,9 @@ __device__ __forceinline__ void tile_body(const FcArgs& a, uint8_t* sa, int e, i
     for (int i = 0; i < 4; ++i) {
       const int r = 16 * mb + 4 * q + i;
       if (r >= rows) continue;
-      float* orow = static_cast<float*>(a.out) + (size_t)(row0 + r) * a.ldo;
-      {
+      uint16_t* orow = static_cast<uint16_t*>(a.out) + (size_t)(row0 + r) * a.ldo;
 #pragma unroll
-        for (int j = 0; j < kNBW; ++j) orow[(size_t)(nb0 + j) * kTileN + rl] = acc[mb][j][i];
-      }
+      for (int j = 0; j < kNBW; ++j) orow[(size_t)(nb0 + j) * kTileN + rl] = f32_to_bf16_rne(acc[mb][j][i]);
     }
   }
 }

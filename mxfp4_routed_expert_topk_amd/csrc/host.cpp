@@ -379,8 +379,9 @@ moe_status forward_with_layout(moe_mxfp4_plan_s* p, const Layout& L, const uint1
            "FC2 launch");
   REC(3);
 
-  CHK(moe::launch_combine(reinterpret_cast<const float*>(ws + L.ws_y), ro.rowpos, topk_ids, topk_weights, T, L.k,
-                          L.H, L.E, acc_fp32, out_bf16, stream), "combine launch");
+  // the prefill kernels land y in bf16, the decode kernels in fp32
+  CHK(moe::launch_combine(ws + L.ws_y, prefill || prefill_mx, ro.rowpos, topk_weights, T, L.k, L.H, acc_fp32,
+                          out_bf16, stream), "combine launch");
   REC(4);
 #undef REC
 #undef CHK

@@ -174,9 +174,9 @@ hipError_t launch_probe_mfma(int kind, int iters, float* sink, int grid, double*
 hipError_t launch_probe_mfma_blocks(const uint8_t* a, const uint8_t* b, const uint8_t* sa, const uint8_t* sb,
                                     const float* c, float* d, int n, hipStream_t stream);
 
-hipError_t launch_combine(const float* y, const int32_t* rowpos, const int32_t* ids,
-                          const float* w, int32_t T, int32_t k, int32_t H, int32_t E,
-                          float* acc, uint16_t* out, hipStream_t stream);
+// y: per-route output rows, fp32 or (y_bf16) bf16.
+hipError_t launch_combine(const void* y, bool y_bf16, const int32_t* rowpos, const float* w, int32_t T, int32_t k,
+                          int32_t H, float* acc, uint16_t* out, hipStream_t stream);
 
 // ---------------------------------------------------------------- device helpers
 #if defined(__HIPCC__)
