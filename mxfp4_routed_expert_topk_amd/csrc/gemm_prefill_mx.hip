@@ -260,6 +260,16 @@ __device__ __forceinline__ void tile_body(const FcArgs& a, uint8_t* sa, int e, i
     // 16 + rl).  Its amax is reduced over those lanes; every lane shuffles, so
     // the stores alone are guarded by the row count.
     static_assert(kNBW == 4, "one 32-column scale block of h per wave");
+    // The codes go through the wave's 4 KB of the (now idle) stage ring and
+    // leave as 16-byte row chunks: stored from the MFMA layout they would be
+    // byte stores, 16 bytes of a row per store, which measured 12 % of FC1.
+    // The barrier finds every wave done reading the ring.
+    static_assert(kWaves * 4096 <= kBufs * kStageBytes && MB * 16 * 32 <= 4096, "code staging fits the ring");
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    uint8_t* const stg = sa + wave * 4096;                   // [MB * 16][32] E4M3
     const int hc = (nb0 / 2) * kTileN;   // first h column of the block
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
@@ -273,13 +283,17 @@ __device__ __forceinline__ void tile_body(const FcArgs& a, uint8_t* sa, int e, i
         for (int d = 1; d < 16; d <<= 1) m = fmaxf(m, __shfl_xor(m, d, kWave));
         const int ex = mx_scale_exp(m);
         const float inv = __uint_as_float((uint32_t)(127 - ex) << 23);   // 2^-e
-        if (r < rows) {
-          uint8_t* crow = a.out_codes + (size_t)(row0 + r) * a.ldo + hc;
-          crow[rl] = (uint8_t)e4m3_rne(h0 * inv);
-          crow[16 + rl] = (uint8_t)e4m3_rne(h1 * inv);
-          if (rl == 0) a.out_scales[(size_t)(row0 + r) * (a.ldo / 32) + hc / 32] = (uint8_t)(ex + 127);
-        }
+        stg[r * 32 + rl] = (uint8_t)e4m3_rne(h0 * inv);
+        stg[r * 32 + 16 + rl] = (uint8_t)e4m3_rne(h1 * inv);
+        if (r < rows && rl == 0) a.out_scales[(size_t)(row0 + r) * (a.ldo / 32) + hc / 32] = (uint8_t)(ex + 127);
       }
+    }
+    asm volatile("" ::: "memory");
+    for (int k = 0; k < MB / 2; ++k) {                         // 32 rows of 32 B per pass
+      const int rr = k * 32 + (lane >> 1), half = lane & 1;
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stg + rr * 32 + half * 16);
+      if (rr < rows)
+        *(__attribute__((address_space(1))) u32x4_t*)(a.out_codes + (size_t)(row0 + rr) * a.ldo + hc + half * 16) = v;
     }
     return;
   }
