@@ -297,16 +297,40 @@ __device__ __forceinline__ void tile_body(const FcArgs& a, uint8_t* sa, int e, i
     }
     return;
   }
+  // FC2: y rounded to bf16.  The rows go through the wave's share of the
+  // (now idle) stage ring and leave as 16-byte row chunks (stored from the
+  // MFMA layout they would be 2-byte stores, 32 bytes of a row per store);
+  // the barrier finds every wave done reading the ring.
+  constexpr int kShare = kBufs * kStageBytes / kWaves / 4096 * 4096;
+  constexpr int RP = kShare / 128;                     // staged rows of 64 bf16 per pass
+  static_assert(RP % 16 == 0 && RP >= 16, "whole 16-row blocks per pass");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  uint8_t* const stg = sa + wave * kShare;
+  const int c0 = nb0 * kTileN;                         // the wave's first output column
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb) {
+  for (int p0 = 0; p0 < MB * 16; p0 += RP) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 16 * mb + 4 * q + i;
-      if (r >= rows) continue;
-      uint16_t* orow = static_cast<uint16_t*>(a.out) + (size_t)(row0 + r) * a.ldo;
+    for (int mb = p0 / 16; mb < MB && mb < (p0 + RP) / 16; ++mb)
 #pragma unroll
-      for (int j = 0; j < kNBW; ++j) orow[(size_t)(nb0 + j) * kTileN + rl] = f32_to_bf16_rne(acc[mb][j][i]);
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < kNBW; ++j)
+          *reinterpret_cast<uint16_t*>(stg + (16 * mb + 4 * q + i - p0) * 128 + (j * kTileN + rl) * 2) =
+              f32_to_bf16_rne(acc[mb][j][i]);
+    asm volatile("" ::: "memory");
+    const int nrows = min(RP, MB * 16 - p0);
+    for (int k = 0; k < nrows / 8; ++k) {              // 8 rows of 128 B per pass
+      const int rr = k * 8 + (lane >> 3), ch = lane & 7;
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stg + rr * 128 + ch * 16);
+      const int gr = p0 + rr;
+      if (gr < rows)
+        *(__attribute__((address_space(1))) u32x4_t*)(static_cast<uint16_t*>(a.out) + (size_t)(row0 + gr) * a.ldo +
+                                                       c0 + ch * 8) = v;
     }
+    asm volatile("" ::: "memory");
   }
 }
 
