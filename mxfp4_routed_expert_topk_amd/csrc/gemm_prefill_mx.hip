@@ -283,8 +283,9 @@ __device__ __forceinline__ void tile_body(const FcArgs& a, uint8_t* sa, int e, i
         for (int d = 1; d < 16; d <<= 1) m = fmaxf(m, __shfl_xor(m, d, kWave));
         const int ex = mx_scale_exp(m);
         const float inv = __uint_as_float((uint32_t)(127 - ex) << 23);   // 2^-e
-        stg[r * 32 + rl] = (uint8_t)e4m3_rne(h0 * inv);
-        stg[r * 32 + 16 + rl] = (uint8_t)e4m3_rne(h1 * inv);
+        const uint32_t c2 = e4m3_pair(h0 * inv, h1 * inv);
+        stg[r * 32 + rl] = (uint8_t)c2;
+        stg[r * 32 + 16 + rl] = (uint8_t)(c2 >> 8);
         if (r < rows && rl == 0) a.out_scales[(size_t)(row0 + r) * (a.ldo / 32) + hc / 32] = (uint8_t)(ex + 127);
       }
     }

@@ -219,8 +219,7 @@ __device__ __forceinline__ float silu_f32(float z) { return z * __builtin_amdgcn
 // MXFP8 scale rule of the MXFP8 x MXFP4 workload: e = floor(log2(amax / 448)),
 // clamped to [-127, 127], amax = 0 -> -127; the block is scaled by 2^-e,
 // saturated to +-448 and rounded to nearest even E4M3FN (subnormals included);
-// the scale byte is e + 127.  Integer and power-of-two arithmetic on the fp32
-// value only, so the codes do not depend on a hardware converter.
+// the scale byte is e + 127.
 // floor(log2(amax / 448)) for finite amax >= 0, clamped to [-127, 127].
 __device__ __forceinline__ int mx_scale_exp(float amax) {
   const uint32_t u = __float_as_uint(amax);
@@ -231,18 +230,27 @@ __device__ __forceinline__ int mx_scale_exp(float amax) {
   return e < -127 ? -127 : (e > 127 ? 127 : e);
 }
 
-// |a| already scaled; saturate to 448 and round to nearest even E4M3FN,
-// without branches.  Normal range (a >= 2^-6): round the fp32 mantissa to
-// three bits by adding 0x7FFFF plus the lowest kept bit (a carry moves into the
-// exponent), then rebias the exponent from 127 to 7.  Below 2^-6 the step is
-// 2^-9, so the code is a * 512 rounded to nearest even (exact scaling).
-__device__ __forceinline__ uint32_t e4m3_rne(float v) {
-  const uint32_t sign = (__float_as_uint(v) >> 31) << 7;
-  const float a = fminf(fabsf(v), 448.0f);
-  const uint32_t u = __float_as_uint(a);
-  const uint32_t norm = ((u + 0x7FFFFu + ((u >> 20) & 1u)) >> 20) - (120u << 3);
-  const uint32_t sub = (uint32_t)__builtin_rintf(a * 512.0f);
-  return (a < 0.015625f ? sub : norm) | sign;
+// Scaled values -> E4M3FN codes, saturated to +-448 and rounded to nearest
+// even (subnormals included): clamp with v_med3_f32, then v_cvt_pk_fp8_f32
+// converts two values to the low (word_sel false) or high 16 bits of a dword,
+// first value in the lower byte.  Infinities clamp to +-448 like any value
+// beyond it; NaN inputs are outside the contract.  An exhaustive run over
+// every finite fp32 bit pattern gave the same code as the integer rounding
+// (round the fp32 mantissa to three bits with the carry into the exponent,
+// rebias 127 -> 7; below 2^-6 the code is the value times 512 rounded to
+// nearest even), and the quantiser's parity test checks every tie of the
+// E4M3 grid against the oracle.
+__device__ __forceinline__ float e4m3_clamp(float v) { return __builtin_amdgcn_fmed3f(v, -448.0f, 448.0f); }
+
+// codes of a, b in bytes 0, 1 (bits 16..31 zero)
+__device__ __forceinline__ uint32_t e4m3_pair(float a, float b) {
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(e4m3_clamp(a), e4m3_clamp(b), 0, false) & 0xFFFFu;
+}
+
+// codes of a, b, c, d in bytes 0..3
+__device__ __forceinline__ uint32_t e4m3_quad(float a, float b, float c, float d) {
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_clamp(a), e4m3_clamp(b), 0, false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(e4m3_clamp(c), e4m3_clamp(d), lo, true);
 }
 #endif
 

@@ -3,7 +3,7 @@
 // e4m3 activation quant"; commit 53edfa98: per-token-group FP8 quant of the
 // gathered rows and requant of h before W2, with UE8M0 scales).
 //
-// Scale rule: mx_scale_exp / e4m3_rne (moe_internal.h).  With it the block
+// Scale rule: mx_scale_exp / e4m3_quad (moe_internal.h).  With it the block
 // maximum lands in [448, 896) and saturates.
 #include "moe_internal.h"
 
@@ -38,8 +38,7 @@ __global__ __launch_bounds__(kThreads) void quant_bf16(const uint16_t* __restric
   uint32_t out[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    out[i] = e4m3_rne(f[4 * i] * inv) | (e4m3_rne(f[4 * i + 1] * inv) << 8) |
-             (e4m3_rne(f[4 * i + 2] * inv) << 16) | (e4m3_rne(f[4 * i + 3] * inv) << 24);
+    out[i] = e4m3_quad(f[4 * i] * inv, f[4 * i + 1] * inv, f[4 * i + 2] * inv, f[4 * i + 3] * inv);
   }
   uint4* dst = reinterpret_cast<uint4*>(codes + b * 32);
   dst[0] = make_uint4(out[0], out[1], out[2], out[3]);
@@ -68,8 +67,7 @@ __global__ __launch_bounds__(kThreads) void quant_f32(const float* __restrict__ 
   uint32_t out[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    out[i] = e4m3_rne(f[4 * i] * inv) | (e4m3_rne(f[4 * i + 1] * inv) << 8) |
-             (e4m3_rne(f[4 * i + 2] * inv) << 16) | (e4m3_rne(f[4 * i + 3] * inv) << 24);
+    out[i] = e4m3_quad(f[4 * i] * inv, f[4 * i + 1] * inv, f[4 * i + 2] * inv, f[4 * i + 3] * inv);
   }
   uint4* dst = reinterpret_cast<uint4*>(codes + b * 32);
   dst[0] = make_uint4(out[0], out[1], out[2], out[3]);

@@ -884,6 +884,23 @@ def test_mxfp8_quantize_bitexact():
     special[2, :32] = 448.0 * np.ldexp(1.0, np.arange(-16, 16))    # block max exactly 448 * 2^15
     special[2, 32:64] = 446.0                                     # just below 448: e = -1
     special[3, ::7] = -3.0e38
+    # every E4M3 code value, every midpoint between neighbours (a tie, rounded
+    # to the even code) and the bf16 values either side of each midpoint; a
+    # leading 448 in each 32-block pins the scale to 2^0
+    ex, man = np.arange(127) >> 3, np.arange(127) & 7
+    grid = np.where(ex == 0, man * 2.0 ** -9, (1 + man / 8.0) * 2.0 ** (ex - 7))
+    mids = (grid[:-1] + grid[1:]) / 2
+    nxt = lambda v, d: (torch.from_numpy(v.astype(np.float32)).to(torch.bfloat16).view(torch.int16) + d
+                        ).view(torch.bfloat16).float().numpy()
+    vals = np.concatenate([grid, mids, nxt(mids, 1), nxt(mids[1:], -1)])
+    vals = np.concatenate([vals, -vals])
+    ties = np.zeros((2, 7168), np.float32)
+    blk = ties.reshape(-1, 32)
+    blk[:, 0] = 448.0
+    flat = blk[:, 1:].reshape(-1)
+    flat[:vals.size] = vals
+    blk[:, 1:] = flat.reshape(-1, 31)
+    special = np.concatenate([special, ties])
     sp_bits = torch.from_numpy(special).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     xs = np.concatenate([x, sp_bits])
     codes, scales = moe.mxfp8_quantize(G.to_dev(xs).view(torch.bfloat16))
