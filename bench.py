@@ -1,7 +1,7 @@
 """Benchmark of the MXFP4 routed-expert MoE layer on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--m 128] [--no-extra] [--no-cpu]
-                    [--workload decode|prefill1536|fusedsum4096|mxfp8x4096] [--fused]
+                    [--workload decode|prefill1536|fusedsum4096|mxfp8x4096] [--fused] [--no-power]
 
 A step is one moe_mxfp4_forward call (the whole layer: route -> FC1 -> FC2 ->
 weighted sum) over one batch of the decode workload: hidden 7168, intermediate
@@ -22,7 +22,8 @@ Prints ONE JSON line:
  * `layer`: per-step event pairs -- median and p90 with warm caches, and again
    with 1 GiB of other data read between steps (cold: nothing of the last step
    is left in the caches) -- the same steps replayed from captured hipGraphs, per-stage
-   times, and a SHA-256 prefix of the output (input set 0);
+   times, a SHA-256 prefix of the output (input set 0), and the operating point
+   (median board power and shader clock over a one-second loop of steps);
  * `roofline`: the dominant kernel (FC1) timed by HIP events recorded on its
    launch stream, priced against the published peak and against the ceiling
    measured on the same box (`ceilings`: the library's peak micro-benchmarks);
@@ -54,6 +55,7 @@ FP8_PEAK_TFLOPS = 5000.0       # dense fp8 MFMA
 METRIC = "MoE layer tokens/s + % HBM roofline (decode M≤128) / % MFMA peak (prefill)"
 STAGES = ("route", "fc1", "fc2", "combine")
 FLUSH_BYTES = 1 << 30
+SETTLE_S = 0.05                # minimum untimed warm-up of the extra workloads (clock ramp after host work)
 CONTEXT = {
     "pages_full_model_decode_step_ms": {"fused_megamoe": 43.3, "nccl_fixed_chain": 54.6},
     "hardware": "4x GB300 (SM100), expert parallel over 4 GPUs",
@@ -110,10 +112,13 @@ def gpu_state():
 
 
 def ceilings():
-    """Measured peaks on this machine with the library's micro-benchmarks: HBM
-    read (plain and non-temporal 128-bit loads over 4 GiB), copy (2 GiB each
-    way, read + write bytes), and the two MFMA instructions the prefill kernels
-    use."""
+    """Measured peaks on this machine with the library's micro-benchmarks: the two
+    MFMA instructions the prefill kernels use, then HBM read (plain and
+    non-temporal 128-bit loads over 4 GiB) and copy (2 GiB each way, read +
+    write bytes).  Run right before the headline's warm-up: a GPU that idled
+    through the seconds of host-side set-up runs its first ~20 ms of work
+    3-6 % slower while its clocks come back up, which would otherwise fall
+    inside the timed steps."""
     import torch
     import mxfp4_routed_expert_topk_amd as moe
     cus = torch.cuda.get_device_properties(0).multi_processor_count
@@ -133,6 +138,10 @@ def ceilings():
             ts.append(a.elapsed_time(b) * 1e-3)
         return min(ts), r
 
+    for name, kind, iters in (("mfma_bf16_tflops", moe.MOE_PROBE_MFMA_BF16, 4000),
+                              ("mfma_f8f4_tflops", moe.MOE_PROBE_MFMA_F8F4, 8000)):
+        t, fl = timed(lambda: moe.probe_mfma(kind, iters, sink, cus * 4))
+        res[name] = round(fl / t / 1e12, 1)
     buf = torch.ones(4 << 30, dtype=torch.uint8, device="cuda")
     for name, kind in (("hbm_read_gbs", moe.MOE_PROBE_READ), ("hbm_read_nt_gbs", moe.MOE_PROBE_READ_NT)):
         t, _ = timed(lambda: moe.probe_memory(kind, buf, None, sink, cus * 8))
@@ -141,10 +150,6 @@ def ceilings():
     t, _ = timed(lambda: moe.probe_memory(moe.MOE_PROBE_COPY, src, dst, sink, cus * 8))
     res["hbm_copy_gbs"] = round(2 * src.numel() / t / 1e9, 1)
     del buf, src, dst
-    for name, kind, iters in (("mfma_bf16_tflops", moe.MOE_PROBE_MFMA_BF16, 4000),
-                              ("mfma_f8f4_tflops", moe.MOE_PROBE_MFMA_F8F4, 8000)):
-        t, fl = timed(lambda: moe.probe_mfma(kind, iters, sink, cus * 4))
-        res[name] = round(fl / t / 1e12, 1)
     torch.cuda.empty_cache()
     return res
 
@@ -172,6 +177,7 @@ class Batches:
     """`sets` device-resident input sets of one workload at T tokens."""
 
     fused = False   # also time the one-launch forward (--fused)
+    power_s = 1.0   # length of the loop that samples power and clock (0: none, --no-power)
 
     def __init__(self, plan, base, sets, make):
         import torch
@@ -250,13 +256,22 @@ class Batches:
         torch.cuda.synchronize()
         return np.array([a.elapsed_time(b) for a, b in evs])   # ms
 
-    def run(self, steps, warmup):
+    def run(self, steps, warmup, settle_s=0.0):
         """The headline (back-to-back steps, one event pair), then per-step
         pairs warm and cold, stage events (per-kernel times on the launch
-        stream), graph replay, and optionally the one-launch forward."""
+        stream), graph replay, and optionally the one-launch forward.  With
+        `settle_s`, the untimed warm-up goes on past `warmup` steps until that
+        many seconds have passed (the extra workloads: each starts after
+        seconds of host-side input generation, with the GPU's clocks down)."""
         import torch
-        for j in range(warmup):
+        t0 = time.time()
+        j = 0
+        while j < warmup or time.time() - t0 < settle_s:
             self.step(j)
+            j += 1
+            if j >= warmup and settle_s > 0:
+                torch.cuda.synchronize()
+        warmup = j
         start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         start.record()
@@ -286,7 +301,8 @@ class Batches:
                 "layer_bytes": alg[:, 0].mean(), "fc1_bytes": alg[:, 1].mean(), "flops": alg[:, 2].mean(),
                 "graph_ms_per_step": self.run_graph(steps, warmup),
                 "fused_ms_per_step": self.run_fused(steps, warmup) if self.fused else None,
-                "digest": self.digest()}
+                "digest": self.digest(),
+                "operating_point": self.power_loop(self.power_s) if self.power_s > 0 else None}
 
     def digest(self):
         """SHA-256 prefix of the outputs of input set 0 (bf16 out, and the fp32
@@ -299,6 +315,60 @@ class Batches:
         if self.acc is not None:
             h.update(self.acc.view(torch.uint8).cpu().numpy().tobytes())
         return h.hexdigest()[:16]
+
+    def power_loop(self, seconds):
+        """Steps back to back for `seconds` while a thread reads the board power
+        and the current shader clock level from sysfs every 20 ms: the operating
+        point the timed legs ran at (a layer that reaches the board's power cap
+        runs at a lower clock).  Medians over the samples after the first
+        quarter of the loop, when the clock has settled."""
+        import threading
+        import torch
+        dev = next((d for d in sorted(glob.glob("/sys/class/drm/card*/device"))
+                    if os.path.exists(os.path.join(d, "pp_dpm_sclk"))), None)
+        if dev is None:
+            return None
+        pw = [f for f in glob.glob(os.path.join(dev, "hwmon", "hwmon*", "power1_*"))
+              if f.endswith(("_input", "_average"))]
+        cap = glob.glob(os.path.join(dev, "hwmon", "hwmon*", "power1_cap"))
+        samples, stop = [], threading.Event()
+
+        def sample():
+            while not stop.is_set():
+                try:
+                    w = int(open(pw[0]).read()) / 1e6 if pw else None
+                    cur = [ln for ln in open(os.path.join(dev, "pp_dpm_sclk")) if ln.strip().endswith("*")]
+                    mhz = float(cur[0].split(":")[1].strip().split("Mhz")[0].split("MHz")[0]) if cur else None
+                    samples.append((time.time(), w, mhz))
+                except (OSError, ValueError, IndexError):
+                    pass
+                stop.wait(0.02)
+
+        torch.cuda.synchronize()
+        th = threading.Thread(target=sample, daemon=True)
+        t0 = time.time()
+        th.start()
+        n = 0
+        while time.time() - t0 < seconds:
+            for j in range(8):
+                self.step(n + j)
+            n += 8
+            torch.cuda.synchronize()
+        t1 = time.time()
+        stop.set()
+        th.join()
+        keep = [x for x in samples if x[0] >= t0 + 0.25 * (t1 - t0)]
+        pws = np.array([x[1] for x in keep if x[1] is not None])
+        mhz = np.array([x[2] for x in keep if x[2] is not None])
+        rec = {"seconds": round(t1 - t0, 2), "steps": n, "us_per_step": round((t1 - t0) / n * 1e6, 1),
+               "samples": len(keep),
+               "power_w_p50": round(float(np.median(pws)), 1) if pws.size else None,
+               "sclk_mhz_p50": round(float(np.median(mhz)), 0) if mhz.size else None}
+        try:
+            rec["power_cap_w"] = round(int(open(cap[0]).read()) / 1e6, 1) if cap else None
+        except (OSError, ValueError):
+            rec["power_cap_w"] = None
+        return rec
 
     def run_fused(self, steps, warmup):
         """The same steps through the one-launch forward (bf16, at most 256
@@ -367,6 +437,8 @@ class Batches:
             out["layer_hbm_frac_of_measured_read"] = round(gbs / ceil["hbm_read_nt_gbs"], 4)
             key = "mfma_f8f4_tflops" if self.base.act == "mxfp8" else "mfma_bf16_tflops"
             out["mfma_frac_of_measured"] = round(tflops / ceil[key], 4)
+        if r.get("operating_point"):
+            out["operating_point"] = r["operating_point"]
         if r.get("fused_ms_per_step"):
             out["fused_us_per_step"] = round(r["fused_ms_per_step"] * 1e3, 2)
             out["fused_tokens_per_s"] = round(self.T / (r["fused_ms_per_step"] * 1e-3), 1)
@@ -452,13 +524,14 @@ def base_line(args, r, summ, config):
             "scaling": "weak", "vs_baseline": None, "data": "synthetic", "config": config, "layer": summ}
 
 
-def prefill_line(args, ceil):
+def prefill_line(args, measured_ceilings):
     """The JSON line of one prefill configuration (see --workload)."""
     import workloads as W
     cid = PREFILL[args.workload]
     case = W.config_case(cid)
     pl, _ = build_plan(cid, case.shape.tokens)
     b = Batches.config(pl, cid, None, 2)
+    ceil = measured_ceilings()
     r = b.run(args.steps, args.warmup)
     summ = b.summary(r, ceil)
     mx = case.act == "mxfp8"
@@ -485,6 +558,7 @@ def prefill_line(args, ceil):
         line["roofline"]["measured_peak"] = ceil[key]
         line["roofline"]["frac_of_measured"] = round(fc1_tflops / ceil[key], 4)
     pl.close()
+    line["_ceil"] = ceil
     return line
 
 
@@ -501,6 +575,8 @@ def main():
     p.add_argument("--workload", default="decode", choices=["decode"] + list(PREFILL))
     p.add_argument("--fused", action="store_true",
                    help="also time the one-launch (cooperative) fused forward on decode batches")
+    p.add_argument("--no-power", action="store_true",
+                   help="skip the one-second loop per workload that samples board power and shader clock")
     p.add_argument("--copy-probe", action="store_true",
                    help="first copy 512 MiB with torch three times: a kernel of known bytes for counter scaling")
     args = p.parse_args()
@@ -524,12 +600,18 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     Batches.fused = args.fused
+    Batches.power_s = 0.0 if args.no_power else 1.0
     state_before = gpu_state()
-    ceil = None if args.no_ceilings else ceilings()
-    if ceil:
-        log(f"measured ceilings: {ceil}")
+
+    def measured_ceilings():
+        c = None if args.no_ceilings else ceilings()
+        if c:
+            log(f"measured ceilings: {c}")
+        return c
+
     if args.workload != "decode":
-        line = prefill_line(args, ceil)
+        line = prefill_line(args, measured_ceilings)
+        ceil = line.pop("_ceil")
         line["ceilings"] = ceil
         line["gpu_state"] = {"before": state_before, "after": gpu_state()}
         line["context"] = CONTEXT
@@ -537,6 +619,7 @@ def main():
         return
     plan, _ = build_plan(1, max(max(W.DECODE_M), args.m))
     head_b = Batches.config(plan, 1, args.m, args.sets)
+    ceil = measured_ceilings()
     r = head_b.run(args.steps, args.warmup)
     head = head_b.summary(r, ceil)
     log(f"decode M={args.m}: {head}")
@@ -563,7 +646,7 @@ def main():
             if m == args.m:
                 continue
             b = Batches.config(plan, 1, m, args.sets)
-            extra[f"decode_m{m}"] = b.summary(b.run(max(20, args.steps), args.warmup), ceil)
+            extra[f"decode_m{m}"] = b.summary(b.run(max(20, args.steps), args.warmup, SETTLE_S), ceil)
             log(f"decode M={m}: {extra[f'decode_m{m}']}")
             del b
         plan.close()
@@ -572,7 +655,7 @@ def main():
         for cid in (2, 3, 4):
             pl, case = build_plan(cid, W.config_case(cid).shape.tokens)
             b = Batches.config(pl, cid, None, 2)
-            extra[case.name] = b.summary(b.run(10, 3), ceil)
+            extra[case.name] = b.summary(b.run(10, 3, SETTLE_S), ceil)
             log(f"config {cid} ({case.name}): {extra[case.name]}")
             pl.close()
             del pl, b
@@ -589,7 +672,7 @@ def main():
         log(f"K3 shapes: plan built in {time.time() - t0:.1f}s")
         for m in W.K3_DECODE_M:
             b = Batches.k3(pl, m, args.sets)
-            extra[f"k3_decode_m{m}"] = b.summary(b.run(max(20, args.steps), args.warmup), ceil)
+            extra[f"k3_decode_m{m}"] = b.summary(b.run(max(20, args.steps), args.warmup, SETTLE_S), ceil)
             log(f"K3 decode M={m}: {extra[f'k3_decode_m{m}']}")
             del b
         pl.close()
