@@ -30,7 +30,20 @@ struct AFrag<true> { uint4 lo, hi; uint32_t scale; };  // 32 E4M3 + E8M0 of grou
 
 // FC1's weight loads carry the non-temporal hint (each weight byte is read
 // once); FC2's measured faster as plain loads.
-template <bool FC1, bool MX, int NBW, int P>
+//
+// Two load schedules, the same arithmetic.  PIPE = false: each loop turn
+// computes and reloads its P column blocks under one condition per block,
+// across which the compiler cannot count loads, so each turn starts by
+// waiting for every load in flight (the P blocks then arrive as one burst of
+// adjacent tiles).  PIPE = true: whole groups of P blocks run with no
+// condition (loads past hi fetch block hi - 1 again and go unused) and the
+// last n % P blocks follow with no loads, so each compute waits only for its
+// own block, P blocks deep.  Measured at hidden 7168 / intermediate 2048 /
+// top-8: PIPE 2-5 % faster for the grouped FC2 at every batch size and for
+// the FC2 + sum kernel at four tokens; the burst 1 % faster for FC1 at 128
+// tokens and 7-10 % faster for the per-route FC1 and the FC2 + sum kernel at
+// one token.
+template <bool FC1, bool MX, int NBW, int P, bool PIPE = false>
 __device__ __forceinline__ void dec_kloop(const FcArgs& a, int e, int nb0, long long arow, int lo, int hi,
                                           f32x4_t (&acc)[NBW]) {
   const int lane = threadIdx.x & (kWave - 1);
@@ -104,12 +117,26 @@ __device__ __forceinline__ void dec_kloop(const FcArgs& a, int e, int nb0, long 
   if (n > 0) {
 #pragma unroll
     for (int p = 0; p < P; ++p) load(Wr[p], Sr[p], Ar[p], lo + p);
-    for (int it = 0; it < n; it += P) {
+    if constexpr (PIPE) {
+      int it = 0;
+      for (; it + P <= n; it += P) {
 #pragma unroll
-      for (int p = 0; p < P; ++p) {
-        if (it + p < n) {
+        for (int p = 0; p < P; ++p) {
           compute(Wr[p], Sr[p], Ar[p], lo + it + p);
           load(Wr[p], Sr[p], Ar[p], lo + it + p + P);
+        }
+      }
+#pragma unroll
+      for (int p = 0; p < P - 1; ++p)
+        if (it + p < n) compute(Wr[p], Sr[p], Ar[p], lo + it + p);
+    } else {
+      for (int it = 0; it < n; it += P) {
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+          if (it + p < n) {
+            compute(Wr[p], Sr[p], Ar[p], lo + it + p);
+            load(Wr[p], Sr[p], Ar[p], lo + it + p + P);
+          }
         }
       }
     }

@@ -55,7 +55,7 @@ __global__ __launch_bounds__(kWave * KSPLIT) void fc_dec(FcArgs a) {
   int lo, hi;
   dec_krange<KSPLIT>(a.mat.kb, wave, &lo, &hi);
   f32x4_t acc[NBW];
-  dec_kloop<FC1, MX, NBW, P>(a, e, nb0, arow, lo, hi, acc);
+  dec_kloop<FC1, MX, NBW, P, !FC1>(a, e, nb0, arow, lo, hi, acc);
 
   // every wave parks its partial sums; the epilogue adds them in wave order
   __shared__ float red[KSPLIT][NBW][4][kWave];

@@ -52,7 +52,7 @@ __global__ __launch_bounds__(kWave * kSumWaves) void fc2_sum(FcArgs a, const flo
     int lo, hi;
     dec_krange<KS>(a.mat.kb, p, &lo, &hi);
     f32x4_t acc[NBW];
-    dec_kloop<false, false, NBW, kSumP>(a, e, nb0, (long long)(f0 + s), lo, hi, acc);
+    dec_kloop<false, false, NBW, kSumP, (NBW > 2)>(a, e, nb0, (long long)(f0 + s), lo, hi, acc);
     if (lane < kTileN)                                  // D row 0: lanes 0..15 hold a block's 16 columns
 #pragma unroll
       for (int j = 0; j < NBW; ++j) red[p][s][j * kTileN + lane] = acc[j][0];
