@@ -22,8 +22,10 @@ Prints ONE JSON line:
  * `layer`: per-step event pairs -- median and p90 with warm caches, and again
    with 1 GiB of other data read between steps (cold: nothing of the last step
    is left in the caches) -- the same steps replayed from captured hipGraphs, per-stage
-   times, a SHA-256 prefix of the output (input set 0), and the operating point
-   (median board power and shader clock over a one-second loop of steps);
+   times, a SHA-256 prefix of the output (input set 0), the operating point
+   (median board power and shader clock over a one-second loop of steps), and
+   for batches of up to 16 tokens the stream floor (the layer's bytes read by
+   the library's read probe in as many launches as the forward makes);
  * `roofline`: the dominant kernel (FC1) timed by HIP events recorded on its
    launch stream, priced against the published peak and against the ceiling
    measured on the same box (`ceilings`: the library's peak micro-benchmarks);
@@ -56,6 +58,7 @@ METRIC = "MoE layer tokens/s + % HBM roofline (decode M≤128) / % MFMA peak (pr
 STAGES = ("route", "fc1", "fc2", "combine")
 FLUSH_BYTES = 1 << 30
 SETTLE_S = 0.05                # minimum untimed warm-up of the extra workloads (clock ramp after host work)
+FLOOR_BYTES = 2 << 30          # source of the stream-floor probe: revisited only after 2 GiB of other reads
 CONTEXT = {
     "pages_full_model_decode_step_ms": {"fused_megamoe": 43.3, "nccl_fixed_chain": 54.6},
     "hardware": "4x GB300 (SM100), expert parallel over 4 GPUs",
@@ -302,6 +305,7 @@ class Batches:
                 "graph_ms_per_step": self.run_graph(steps, warmup),
                 "fused_ms_per_step": self.run_fused(steps, warmup) if self.fused else None,
                 "digest": self.digest(),
+                "stream_floor_us": self.stream_floor(),
                 "operating_point": self.power_loop(self.power_s) if self.power_s > 0 else None}
 
     def digest(self):
@@ -315,6 +319,50 @@ class Batches:
         if self.acc is not None:
             h.update(self.acc.view(torch.uint8).cpu().numpy().tobytes())
         return h.hexdigest()[:16]
+
+    def stream_floor(self, reps=40):
+        """The layer's algorithmic bytes streamed by the library's read probe
+        (non-temporal 128-bit loads) in as many launches as the forward makes
+        -- two up to 32 routes (FC1; FC2 with the sum), else four (route, FC1,
+        FC2, combine; the route and combine launches read 64 KB and the
+        output) -- back to back under one event pair: what a chain of kernels
+        that did nothing but move the layer's bytes reaches at this batch size,
+        launch gaps and ramp included.  Microseconds per layer; small batches
+        only (up to 16 tokens), where launches are a large part of the time."""
+        import torch
+        import mxfp4_routed_expert_topk_amd as moe
+        if self.base.act != "bf16" or self.T > 16:
+            return None
+        w13, w2 = expert_bytes(self.H, self.I)
+        t = float(np.mean(self.touched))
+        R = self.T * self.k
+        fc1 = t * w13 + self.T * self.H * 2
+        fc2 = t * w2 + R * self.I * 2
+        sizes = [fc1, fc2] if R <= 32 else [64 << 10, fc1, fc2, (64 << 10) + self.T * self.H * 2]
+        sizes = [int(b + 4095) // 4096 * 4096 for b in sizes]
+        src = torch.empty(FLOOR_BYTES, dtype=torch.uint8, device="cuda")
+        sink = torch.empty(16384, dtype=torch.float32, device="cuda")
+        grid = torch.cuda.get_device_properties(0).multi_processor_count * 8
+        off = [0]
+
+        def layer():
+            for b in sizes:
+                if off[0] + b > FLOOR_BYTES:
+                    off[0] = 0
+                moe.probe_memory(moe.MOE_PROBE_READ_NT, src[off[0]:off[0] + b], None, sink, grid)
+                off[0] += b
+
+        for _ in range(10):
+            layer()
+        a, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(reps):
+            layer()
+        e.record()
+        torch.cuda.synchronize()
+        del src
+        return a.elapsed_time(e) / reps * 1e3
 
     def power_loop(self, seconds):
         """Steps back to back for `seconds` while a thread reads the board power
@@ -437,6 +485,9 @@ class Batches:
             out["layer_hbm_frac_of_measured_read"] = round(gbs / ceil["hbm_read_nt_gbs"], 4)
             key = "mfma_f8f4_tflops" if self.base.act == "mxfp8" else "mfma_bf16_tflops"
             out["mfma_frac_of_measured"] = round(tflops / ceil[key], 4)
+        if r.get("stream_floor_us"):
+            out["stream_floor_us"] = round(r["stream_floor_us"], 2)
+            out["frac_of_stream_floor"] = round(r["stream_floor_us"] / (ms * 1e3), 4)
         if r.get("operating_point"):
             out["operating_point"] = r["operating_point"]
         if r.get("fused_ms_per_step"):

@@ -21,6 +21,11 @@
 
 namespace moe {
 
+// Largest K range of one wave, in 128-K column blocks: K <= kMaxDimension and
+// the K split (dec_ksplit) is four ranges from kKsplit4Blocks blocks up.
+constexpr int kMaxStagedBlocks = (kMaxDimension / kTileK + 3) / 4;
+static_assert((kKsplit4Blocks + 1) / 2 <= kMaxStagedBlocks, "two ranges below the four-range threshold fit too");
+
 template <bool MX>
 struct AFrag;
 template <>
@@ -43,9 +48,17 @@ struct AFrag<true> { uint4 lo, hi; uint32_t scale; };  // 32 E4M3 + E8M0 of grou
 // the FC2 + sum kernel at four tokens; the burst 1 % faster for FC1 at 128
 // tokens and 7-10 % faster for the per-route FC1 and the FC2 + sum kernel at
 // one token.
-template <bool FC1, bool MX, int NBW, int P, bool PIPE = false>
+//
+// ALDS (bf16 only): every lane's A row is the same row (one route per tile).
+// Loaded per lane, each column block took four 1 KB load instructions for
+// 256 distinct bytes; instead the wave copies its K range of the row to its
+// own LDS region `alds` (n * 256 bytes) once, in 1 KB loads issued ahead of
+// the weight prologue, and reads the fragments from there (16-lane broadcast
+// reads).  Only this wave touches its region, so no barrier is needed.
+template <bool FC1, bool MX, int NBW, int P, bool PIPE = false, bool ALDS = false>
 __device__ __forceinline__ void dec_kloop(const FcArgs& a, int e, int nb0, long long arow, int lo, int hi,
-                                          f32x4_t (&acc)[NBW]) {
+                                          f32x4_t (&acc)[NBW], uint8_t* alds = nullptr) {
+  static_assert(!(ALDS && MX), "the staged row is bf16");
   const int lane = threadIdx.x & (kWave - 1);
   const int kq = lane >> 4;
   const MatLayout M = a.mat;
@@ -62,7 +75,7 @@ __device__ __forceinline__ void dec_kloop(const FcArgs& a, int e, int nb0, long 
   uint32_t Sr[P][NBW];
   AFrag<MX> Ar[P];
 
-  auto load = [&](uint4 (&w)[NBW], uint32_t (&s)[NBW], AFrag<MX>& af, int kb) {
+  auto load_w = [&](uint4 (&w)[NBW], uint32_t (&s)[NBW], int kb) {
     kb = min(kb, hi - 1);
 #pragma unroll
     for (int j = 0; j < NBW; ++j) {
@@ -76,7 +89,14 @@ __device__ __forceinline__ void dec_kloop(const FcArgs& a, int e, int nb0, long 
       }
       s[j] = *reinterpret_cast<const uint32_t*>(sbase + j * sstride + (size_t)(kb >> 2) * kScaleGroupBytes);
     }
-    if constexpr (!MX) {
+  };
+  auto load_a = [&](AFrag<MX>& af, int kb) {
+    kb = min(kb, hi - 1);
+    if constexpr (ALDS) {
+      const uint4* ap = reinterpret_cast<const uint4*>(alds + (kb - lo) * (kTileK * 2) + kq * 64);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) af.v[q] = ap[q];
+    } else if constexpr (!MX) {
       const uint4* ap = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.a) + arow * a.lda +
                                                        (size_t)kb * kTileK + kq * 32);
 #pragma unroll
@@ -87,6 +107,10 @@ __device__ __forceinline__ void dec_kloop(const FcArgs& a, int e, int nb0, long 
       af.hi = *reinterpret_cast<const uint4*>(ap + 64);
       af.scale = a.a_scales[arow * (a.lda / 32) + kb * 4 + kq];
     }
+  };
+  auto load = [&](uint4 (&w)[NBW], uint32_t (&s)[NBW], AFrag<MX>& af, int kb) {
+    load_w(w, s, kb);
+    load_a(af, kb);
   };
 
   auto compute = [&](const uint4 (&w)[NBW], const uint32_t (&s)[NBW], const AFrag<MX>& af, int kb) {
@@ -115,8 +139,32 @@ __device__ __forceinline__ void dec_kloop(const FcArgs& a, int e, int nb0, long 
   };
 
   if (n > 0) {
+    if constexpr (ALDS) {
+      // the row's bytes [lo, hi) * 256 in 1 KB loads (a fixed count: chunks past
+      // the range are clamped to its last 16 bytes, read and written again
+      // with the same value, so no load or write sits behind a condition),
+      // then the weight loads of the prologue, then the LDS writes, which wait
+      // only for the row's loads
+      constexpr int kRowLoads = kMaxStagedBlocks * kTileK * 2 / 1024;
+      const int nbytes = n * kTileK * 2;
+      const uint8_t* row = static_cast<const uint8_t*>(a.a) + (arow * a.lda + (long long)lo * kTileK) * 2;
+      uint4 st[kRowLoads];
+      int off[kRowLoads];
 #pragma unroll
-    for (int p = 0; p < P; ++p) load(Wr[p], Sr[p], Ar[p], lo + p);
+      for (int i = 0; i < kRowLoads; ++i) {
+        off[i] = min(i * 1024 + lane * 16, nbytes - 16);
+        st[i] = *reinterpret_cast<const uint4*>(row + off[i]);
+      }
+#pragma unroll
+      for (int p = 0; p < P; ++p) load_w(Wr[p], Sr[p], lo + p);
+#pragma unroll
+      for (int i = 0; i < kRowLoads; ++i) *reinterpret_cast<uint4*>(alds + off[i]) = st[i];
+#pragma unroll
+      for (int p = 0; p < P; ++p) load_a(Ar[p], lo + p);
+    } else {
+#pragma unroll
+      for (int p = 0; p < P; ++p) load(Wr[p], Sr[p], Ar[p], lo + p);
+    }
     if constexpr (PIPE) {
       int it = 0;
       for (; it + P <= n; it += P) {

@@ -55,7 +55,16 @@ __global__ __launch_bounds__(kWave * KSPLIT) void fc_dec(FcArgs a) {
   int lo, hi;
   dec_krange<KSPLIT>(a.mat.kb, wave, &lo, &hi);
   f32x4_t acc[NBW];
-  dec_kloop<FC1, MX, NBW, P, !FC1>(a, e, nb0, arow, lo, hi, acc);
+  if constexpr (PER_ROUTE && !MX) {
+    // one token row per tile: each wave stages its K range of it in its own
+    // share of the dynamic LDS (launch_dec sizes it: KSPLIT ranges); measured
+    // FC1 21.4 -> 19.0 us at one token, 58.5 -> 51.3 us at four
+    extern __shared__ __align__(16) uint8_t row_lds[];
+    const int per = (a.mat.kb + KSPLIT - 1) / KSPLIT;
+    dec_kloop<FC1, MX, NBW, P, !FC1, true>(a, e, nb0, arow, lo, hi, acc, row_lds + wave * per * (kTileK * 2));
+  } else {
+    dec_kloop<FC1, MX, NBW, P, !FC1>(a, e, nb0, arow, lo, hi, acc);
+  }
 
   // every wave parks its partial sums; the epilogue adds them in wave order
   __shared__ float red[KSPLIT][NBW][4][kWave];
@@ -101,7 +110,8 @@ __global__ __launch_bounds__(kWave * KSPLIT) void fc_dec(FcArgs a) {
 template <bool FC1, bool MX, int NBW, int KSPLIT, int P, bool PER_ROUTE>
 hipError_t launch_dec(const FcArgs& a, int tiles_max, hipStream_t stream) {
   const dim3 grid(a.mat.nb / NBW, tiles_max);
-  hipLaunchKernelGGL((fc_dec<FC1, MX, NBW, KSPLIT, P, PER_ROUTE>), grid, dim3(kWave * KSPLIT), 0, stream, a);
+  const size_t lds = PER_ROUTE && !MX ? (size_t)KSPLIT * ((a.mat.kb + KSPLIT - 1) / KSPLIT) * kTileK * 2 : 0;
+  hipLaunchKernelGGL((fc_dec<FC1, MX, NBW, KSPLIT, P, PER_ROUTE>), grid, dim3(kWave * KSPLIT), lds, stream, a);
   return hipGetLastError();
 }
 
