@@ -25,7 +25,7 @@
 namespace moe {
 namespace {
 
-template <bool FC1, bool MX, int NBW, int KSPLIT, int P, bool PER_ROUTE>
+template <bool FC1, bool MX, int NBW, int KSPLIT, int P, bool PER_ROUTE, bool GRP>
 __global__ __launch_bounds__(kWave * KSPLIT) void fc_dec(FcArgs a) {
   static_assert(!FC1 || NBW % 2 == 0, "FC1 groups hold gate/up pairs");
   const int tile = blockIdx.y;
@@ -60,10 +60,10 @@ __global__ __launch_bounds__(kWave * KSPLIT) void fc_dec(FcArgs a) {
     // share of the dynamic LDS (launch_dec sizes it: KSPLIT ranges); measured
     // FC1 21.4 -> 19.0 us at one token, 58.5 -> 51.3 us at four
     extern __shared__ __align__(16) uint8_t row_lds[];
-    const int per = (a.mat.kb + KSPLIT - 1) / KSPLIT;
-    dec_kloop<FC1, MX, NBW, P, !FC1, true>(a, e, nb0, arow, lo, hi, acc, row_lds + wave * per * (kTileK * 2));
+    const int per = dec_krange_max(a.mat.kb, KSPLIT);
+    dec_kloop<FC1, MX, NBW, P, !FC1, true, GRP>(a, e, nb0, arow, lo, hi, acc, row_lds + wave * per * (kTileK * 2));
   } else {
-    dec_kloop<FC1, MX, NBW, P, !FC1>(a, e, nb0, arow, lo, hi, acc);
+    dec_kloop<FC1, MX, NBW, P, !FC1, false, GRP>(a, e, nb0, arow, lo, hi, acc);
   }
 
   // every wave parks its partial sums; the epilogue adds them in wave order
@@ -110,8 +110,15 @@ __global__ __launch_bounds__(kWave * KSPLIT) void fc_dec(FcArgs a) {
 template <bool FC1, bool MX, int NBW, int KSPLIT, int P, bool PER_ROUTE>
 hipError_t launch_dec(const FcArgs& a, int tiles_max, hipStream_t stream) {
   const dim3 grid(a.mat.nb / NBW, tiles_max);
-  const size_t lds = PER_ROUTE && !MX ? (size_t)KSPLIT * ((a.mat.kb + KSPLIT - 1) / KSPLIT) * kTileK * 2 : 0;
-  hipLaunchKernelGGL((fc_dec<FC1, MX, NBW, KSPLIT, P, PER_ROUTE>), grid, dim3(kWave * KSPLIT), lds, stream, a);
+  const size_t lds = PER_ROUTE && !MX ? (size_t)KSPLIT * dec_krange_max(a.mat.kb, KSPLIT) * kTileK * 2 : 0;
+  // whole scale groups per K range: FC1 takes the group schedule (one scale
+  // load per four column blocks; measured 6 % faster FC1 at 128 tokens, 2-7 %
+  // faster layers from 1 to 128 tokens); the grouped FC2 measured 2 % slower
+  // with it and keeps the pipelined one
+  if (FC1 && a.mat.kb % 4 == 0)
+    hipLaunchKernelGGL((fc_dec<FC1, MX, NBW, KSPLIT, P, PER_ROUTE, true>), grid, dim3(kWave * KSPLIT), lds, stream, a);
+  else
+    hipLaunchKernelGGL((fc_dec<FC1, MX, NBW, KSPLIT, P, PER_ROUTE, false>), grid, dim3(kWave * KSPLIT), lds, stream, a);
   return hipGetLastError();
 }
 

@@ -31,7 +31,7 @@ namespace {
 constexpr int kSumWaves = 8;
 constexpr int kSumP = 2;
 
-template <int KS, int NBW>
+template <int KS, int NBW, bool GRP>
 __global__ __launch_bounds__(kWave * kSumWaves) void fc2_sum(FcArgs a, const float* __restrict__ w, int H,
                                                             float* __restrict__ acc_out, uint16_t* __restrict__ out) {
   __shared__ float red[KS][kMaxTopK][NBW * kTileN];  // k <= kMaxTopK
@@ -46,7 +46,7 @@ __global__ __launch_bounds__(kWave * kSumWaves) void fc2_sum(FcArgs a, const flo
   // a unit's h row segment, staged by its wave (launch_sum sizes this: one K
   // range per wave)
   extern __shared__ __align__(16) uint8_t row_lds[];
-  const int per = (a.mat.kb + KS - 1) / KS;
+  const int per = dec_krange_max(a.mat.kb, KS);
   for (int u = wave; u < units; u += kSumWaves) {
     const int vi = u / KS, p = u - vi * KS;
     uint64_t rest = valid;
@@ -59,8 +59,8 @@ __global__ __launch_bounds__(kWave * kSumWaves) void fc2_sum(FcArgs a, const flo
     // one token: the unit's h row segment staged in LDS (1-token layer 13.6 ->
     // 13.2 us in this kernel); at four tokens the per-lane loads measured
     // 0.7 us faster
-    dec_kloop<false, false, NBW, kSumP, (NBW > 2), (NBW == 2)>(a, e, nb0, (long long)(f0 + s), lo, hi, acc,
-                                                               row_lds + wave * per * (kTileK * 2));
+    dec_kloop<false, false, NBW, kSumP, (NBW > 2), (NBW == 2), GRP>(a, e, nb0, (long long)(f0 + s), lo, hi, acc,
+                                                                    row_lds + wave * per * (kTileK * 2));
     if (lane < kTileN)                                  // D row 0: lanes 0..15 hold a block's 16 columns
 #pragma unroll
       for (int j = 0; j < NBW; ++j) red[p][s][j * kTileN + lane] = acc[j][0];
@@ -87,11 +87,15 @@ hipError_t launch_sum(const FcArgs& a, const float* weights, int32_t T, int32_t 
                       hipStream_t stream) {
   const dim3 grid(a.mat.nb / NBW, T), block(kWave * kSumWaves);
   const int ks = dec_ksplit(a.mat.kb);
-  const size_t lds = NBW == 2 ? (size_t)kSumWaves * ((a.mat.kb + ks - 1) / ks) * kTileK * 2 : 0;
-  if (ks == 4)
-    hipLaunchKernelGGL((fc2_sum<4, NBW>), grid, block, lds, stream, a, weights, H, acc, out);
-  else
-    hipLaunchKernelGGL((fc2_sum<2, NBW>), grid, block, lds, stream, a, weights, H, acc, out);
+  const size_t lds = NBW == 2 ? (size_t)kSumWaves * dec_krange_max(a.mat.kb, ks) * kTileK * 2 : 0;
+  const bool grp = a.mat.kb % 4 == 0;   // whole scale groups per K range
+  if (ks == 4) {
+    if (grp) hipLaunchKernelGGL((fc2_sum<4, NBW, true>), grid, block, lds, stream, a, weights, H, acc, out);
+    else hipLaunchKernelGGL((fc2_sum<4, NBW, false>), grid, block, lds, stream, a, weights, H, acc, out);
+  } else {
+    if (grp) hipLaunchKernelGGL((fc2_sum<2, NBW, true>), grid, block, lds, stream, a, weights, H, acc, out);
+    else hipLaunchKernelGGL((fc2_sum<2, NBW, false>), grid, block, lds, stream, a, weights, H, acc, out);
+  }
   return hipGetLastError();
 }
 
