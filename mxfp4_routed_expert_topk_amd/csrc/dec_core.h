@@ -52,7 +52,7 @@ struct AFrag<true> { uint4 lo, hi; uint32_t scale; };  // 32 E4M3 + E8M0 of grou
 // per turn, the group's scale dwords loaded once, with its first block (a
 // lane's scale dword covers the four blocks of a group: loading it with every
 // block moved four times the scale bytes through the load path); measured
-// FC1 548 -> 515 us at 128 tokens, 18.5 -> 18.1 us per-route at one token.
+// FC1 548 -> 515 us and FC2 287 -> 278 us at 128 tokens.
 //
 // ALDS (bf16 only): every lane's A row is the same row (one route per tile).
 // Loaded per lane, each column block took four 1 KB load instructions for

@@ -111,11 +111,10 @@ template <bool FC1, bool MX, int NBW, int KSPLIT, int P, bool PER_ROUTE>
 hipError_t launch_dec(const FcArgs& a, int tiles_max, hipStream_t stream) {
   const dim3 grid(a.mat.nb / NBW, tiles_max);
   const size_t lds = PER_ROUTE && !MX ? (size_t)KSPLIT * dec_krange_max(a.mat.kb, KSPLIT) * kTileK * 2 : 0;
-  // whole scale groups per K range: FC1 takes the group schedule (one scale
-  // load per four column blocks; measured 6 % faster FC1 at 128 tokens, 2-7 %
-  // faster layers from 1 to 128 tokens); the grouped FC2 measured 2 % slower
-  // with it and keeps the pipelined one
-  if (FC1 && a.mat.kb % 4 == 0)
+  // whole scale groups per K range: the group schedule (one scale load per
+  // four column blocks; measured 6 % faster FC1 and 3 % faster FC2 at 128
+  // tokens, 2-7 % faster layers from 1 to 128 tokens)
+  if (a.mat.kb % 4 == 0)
     hipLaunchKernelGGL((fc_dec<FC1, MX, NBW, KSPLIT, P, PER_ROUTE, true>), grid, dim3(kWave * KSPLIT), lds, stream, a);
   else
     hipLaunchKernelGGL((fc_dec<FC1, MX, NBW, KSPLIT, P, PER_ROUTE, false>), grid, dim3(kWave * KSPLIT), lds, stream, a);
@@ -136,12 +135,12 @@ hipError_t launch_sched(const FcArgs& a, int tiles_max, hipStream_t stream) {
 // 128).  Up to 4 tokens: two row blocks per workgroup, two column blocks
 // loaded ahead; larger batches: four row blocks (measured 9-10 % faster than
 // two from 8 to 16 tokens; eight FC1 row blocks, or three column blocks ahead,
-// were slower there), eight for FC2 above 16 tokens.
+// were slower there; with the group schedule four FC2 row blocks also beat
+// eight by 3-4 % at 64 and 128 tokens).
 template <bool FC1, bool MX>
 hipError_t launch_fc(const FcArgs& a, int tiles_max, int tokens, hipStream_t stream) {
   if (tokens <= kSmallTokens) return launch_sched<FC1, MX, 2, 2>(a, tiles_max, stream);
-  if (FC1 || tokens <= 16) return launch_sched<FC1, MX, 4, 2>(a, tiles_max, stream);
-  return launch_sched<FC1, MX, 8, 2>(a, tiles_max, stream);
+  return launch_sched<FC1, MX, 4, 2>(a, tiles_max, stream);
 }
 
 }  // namespace
