@@ -149,6 +149,13 @@ __device__ __forceinline__ void tile_body(const FcArgs& a, uint8_t* sa, int e, i
   constexpr int kRing = kDepth + 1;
   u32x4_t bq[kRing][kNBW];
   uint32_t bs[kRing][kNBW];
+  // A lane's scale dword covers the four stages of a group.  With a ring of
+  // four slots (slot = stage % 4) only slot 0 holds a group's first stage: it
+  // alone loads scales, and they are kept in `gsc` for the group's four stages
+  // (loaded with every stage they moved four times the bytes through the load
+  // path).  Other ring sizes load them with every stage.
+  constexpr bool kGroupScales = kRing % 4 == 0;
+  uint32_t gsc[kNBW];
 
   // Stage s >= S (the loads issued "past the end", see run_stage): the
   // per-lane offset is set to kPastEnd and the scalar one to 0, which puts the
@@ -171,7 +178,7 @@ __device__ __forceinline__ void tile_body(const FcArgs& a, uint8_t* sa, int e, i
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rascl, (lds_void_t*)(buf + kStageA + kScaleLanes * 4 * wave), 4,
                                                real ? soff : kPastEnd, real ? 4 * s : 0, 0, 0);
   };
-  auto load_regs = [&](u32x4_t (&q)[kNBW], uint32_t (&sb)[kNBW], int s) {
+  auto load_regs = [&](u32x4_t (&q)[kNBW], uint32_t (&sb)[kNBW], int s, bool with_scales) {
     const bool real = s < S;
 #pragma unroll
     for (int j = 0; j < kNBW; ++j)
@@ -183,10 +190,12 @@ __device__ __forceinline__ void tile_body(const FcArgs& a, uint8_t* sa, int e, i
     // Past the end: the last stage's dword again (an out-of-range offset here
     // makes the compiler branch around the loads, and its waits then count
     // the loads of later stages too).
-    const int sg = (min(s, S - 1) >> 2) * kScaleGroupBytes;
+    if (with_scales) {
+      const int sg = (min(s, S - 1) >> 2) * kScaleGroupBytes;
 #pragma unroll
-    for (int j = 0; j < kNBW; ++j)
-      sb[j] = __builtin_amdgcn_raw_buffer_load_b32(rscale, lane * 4, j * sstride + sg, 0);
+      for (int j = 0; j < kNBW; ++j)
+        sb[j] = __builtin_amdgcn_raw_buffer_load_b32(rscale, lane * 4, j * sstride + sg, 0);
+    }
   };
 
   // A operand position of this lane inside a staged 16-row block
@@ -205,12 +214,22 @@ __device__ __forceinline__ void tile_body(const FcArgs& a, uint8_t* sa, int e, i
     // this wave's loads of stage st have landed (the kDepth - 1 groups after
     // it may still be in flight) and its LDS reads of stage st-1 have
     // returned; the barrier extends both to every wave
-    MOE_WAIT_VM_LGKM((kDepth - 1) * (NA + 1 + 2 * kNBW));
+    constexpr int kLater = [] {   // loads of the kDepth - 1 groups issued after stage st's
+      int n = 0;
+      for (int d = 1; d < kDepth; ++d) n += NA + 1 + kNBW + (!kGroupScales || (p + d) % 4 == 0 ? kNBW : 0);
+      return n;
+    }();
+    MOE_WAIT_VM_LGKM(kLater);
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     issue_lds((st + kDepth) % kRing, st + kDepth);   // into the buffer of stage st-1
-    load_regs(bq[(p + kDepth) % kRing], bs[(p + kDepth) % kRing], st + kDepth);
+    load_regs(bq[(p + kDepth) % kRing], bs[(p + kDepth) % kRing], st + kDepth,
+              !kGroupScales || (p + kDepth) % 4 == 0);
+    if constexpr (kGroupScales && p % 4 == 0) {
+#pragma unroll
+      for (int j = 0; j < kNBW; ++j) gsc[j] = bs[p][j];
+    }
     const uint8_t* cur = sa + (st % kRing) * kStageBytes;
     const int sh = 8 * (st & 3);
     const uint8_t* curs = cur + kStageA;
@@ -225,7 +244,7 @@ __device__ __forceinline__ void tile_body(const FcArgs& a, uint8_t* sa, int e, i
       for (int j = 0; j < kNBW; ++j) {
         const i32x8_t Bf = {(int)bq[p][j][0], (int)bq[p][j][1], (int)bq[p][j][2], (int)bq[p][j][3], 0, 0, 0, 0};
         acc[mb][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(Af, Bf, acc[mb][j], 0, 4, 0, sc, 0,
-                                                                      (int)((bs[p][j] >> sh) & 0xFFu));
+                                                                      (int)(((kGroupScales ? gsc[j] : bs[p][j]) >> sh) & 0xFFu));
       }
     }
     // The stage's MFMAs stay above the next barrier (this empty statement
@@ -242,7 +261,7 @@ __device__ __forceinline__ void tile_body(const FcArgs& a, uint8_t* sa, int e, i
 #pragma unroll
   for (int d = 0; d < kDepth; ++d) {
     issue_lds(d, d);
-    load_regs(bq[d], bs[d], d);
+    load_regs(bq[d], bs[d], d, !kGroupScales || d % 4 == 0);
     __builtin_amdgcn_sched_barrier(0);
   }
   int s0 = 0;
