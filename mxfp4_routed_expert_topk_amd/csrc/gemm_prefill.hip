@@ -154,19 +154,30 @@ __device__ __forceinline__ void k_loop_r(uint8_t* smem, const uint8_t* const (&s
   constexpr int NJ = 2;
   constexpr int W = C::W;
   constexpr int NA = C::nA_live(LIVE);   // activation copies per wave and stage
-  constexpr int G = NA + 2 * NJ;         // loads per wave and stage
   constexpr int R = D + 1;               // ring slots
+  // A scale dword covers four 128-K blocks, i.e. eight stages; even stages
+  // take the dwords of the tile's lanes 0..31, odd stages those of lanes
+  // 32..63 (the two K halves).  Only ring slot 0 loads them, both halves
+  // (R = 4 or 8 stages per ring pass, a pass lies in one group), and the pass
+  // keeps them in `gsc` (loaded with every stage they moved four to eight
+  // times the bytes through the load path).
+  static_assert(8 % R == 0, "a ring pass lies inside one scale group");
+  // loads per wave of the stage in ring slot `slot`
+  constexpr auto group_size = [](int slot) { return NA + NJ + (slot == 0 ? 2 * NJ : 0); };
+  constexpr int G0 = group_size(0);
   constexpr uint32_t kPastEnd = 0x80000000u;
   constexpr int kSlot = NA * W * 1024;   // the stage's live activation rows
-  static_assert(R * kSlot <= kRingBytes && (D - 1) * G <= 63, "activation ring, vmcnt range");
+  static_assert(R * kSlot <= kRingBytes && (D - 1) * G0 <= 63, "activation ring, vmcnt range");
   const int n32 = lane & 31, h = lane >> 5;
   const int aoff = n32 * (kStageK * 2);
   u32x4_t bc[R][NJ];
-  uint32_t sraw[R][NJ];
+  uint32_t sraw[2][NJ];   // slot 0's scale dwords, [K half][row block pair]
+  uint32_t gsc[2][NJ];    // the current pass's
 
   // loads [first, last) of stage st's group into ring slot `slot`
   auto issue = [&](auto slot_c, int st, int first, int last) {
     constexpr int slot = decltype(slot_c)::value;
+    constexpr int G = group_size(slot);
     const bool real = st < S;
     const int sa = min(st, S - 1);
     uint8_t* buf = smem + slot * kSlot;
@@ -181,9 +192,9 @@ __device__ __forceinline__ void k_loop_r(uint8_t* smem, const uint8_t* const (&s
         bc[slot][nj] = __builtin_amdgcn_raw_buffer_load_b128(rcode, real ? coff[nj] : kPastEnd,
                                                              real ? st * kHalfTile : 0, 0);
       } else {
-        const int nj = c - NA - NJ;
-        sraw[slot][nj] = __builtin_amdgcn_raw_buffer_load_b32(rscale, real ? soff[nj] : kPastEnd,
-                                                              real ? (int)scale_off(st) : 0, 0);
+        const int hf = (c - NA - NJ) / NJ, nj = (c - NA - NJ) % NJ;
+        sraw[hf][nj] = __builtin_amdgcn_raw_buffer_load_b32(rscale, real ? soff[nj] : kPastEnd,
+                                                            real ? (int)scale_off(st + hf) : 0, 0);
       }
     }
   };
@@ -206,7 +217,12 @@ __device__ __forceinline__ void k_loop_r(uint8_t* smem, const uint8_t* const (&s
     // this wave's group of stage st has landed (the D - 1 groups after it may
     // still be in flight) and its LDS reads of stage st - 1 have returned; the
     // barrier extends both to every wave
-    MOE_WAIT_VMCNT((D - 1) * G);
+    constexpr int kLater = [] {   // loads of the D - 1 groups issued after stage st's
+      int n = 0;
+      for (int d = 1; d < D; ++d) n += NA + NJ + ((p + d) % R == 0 ? 2 * NJ : 0);   // group_size((p + d) % R)
+      return n;
+    }();
+    MOE_WAIT_VMCNT(kLater);
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
@@ -227,16 +243,24 @@ __device__ __forceinline__ void k_loop_r(uint8_t* smem, const uint8_t* const (&s
     __builtin_amdgcn_sched_group_barrier(0x100, LIVE, 0);
     __builtin_amdgcn_sched_group_barrier(0x008, NJ * LIVE - 1, 0);
     __builtin_amdgcn_sched_barrier(0);
+    if constexpr (p == 0) {
+#pragma unroll
+      for (int nj = 0; nj < NJ; ++nj) {
+        gsc[0][nj] = sraw[0][nj];
+        gsc[1][nj] = sraw[1][nj];
+      }
+    }
     float bs[NJ];
 #pragma unroll
-    for (int nj = 0; nj < NJ; ++nj) bs[nj] = e8m0_to_f32((sraw[p][nj] >> sh) & 0xFFu);
+    for (int nj = 0; nj < NJ; ++nj) bs[nj] = e8m0_to_f32((gsc[p & 1][nj] >> sh) & 0xFFu);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       bf16x8_t B[NJ];
 #pragma unroll
       for (int nj = 0; nj < NJ; ++nj) B[nj] = dequant8(bc[p][nj][s], bs[nj]);
       acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Ac[0], B[0], acc[0][0], 0, 0, 0);
-      issue(std::integral_constant<int, q>{}, st + D, s * G / 4, (s + 1) * G / 4);
+      constexpr int Gq = group_size(q);
+      issue(std::integral_constant<int, q>{}, st + D, s * Gq / 4, (s + 1) * Gq / 4);
       if (s < 3) {
 #pragma unroll
         for (int mi = 0; mi < LIVE; ++mi)
@@ -268,7 +292,7 @@ __device__ __forceinline__ void k_loop_r(uint8_t* smem, const uint8_t* const (&s
 
   // one group after another: the waits count whole groups in issue order
   auto prologue = [&](auto pc, int st) {
-    issue(pc, st, 0, G);
+    issue(pc, st, 0, group_size(decltype(pc)::value));
     __builtin_amdgcn_sched_barrier(0);
   };
   ring_pass<0, D>(prologue, 0, D);
