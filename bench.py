@@ -686,7 +686,11 @@ def main():
         "bound": "hbm", "achieved": round(fc1_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
         "frac": round(fc1_gbs / HBM_PEAK_GBS, 4),
         "traffic": counter_traffic("decode", "decode_m128") if args.m == 128 else None,
-        "kernel": "fc_dec<true,false,4,4,2,false,true> (FC1, bf16, 16-row tiles, group schedule)", "kernel_us": round(fc1_us, 2),
+        "kernel": ("fc_dec<true,false,4,4,2,false,true,2> (FC1, bf16, 16-row tiles, group schedule, two K "
+                   "ranges per wave)" if args.m >= 32 else
+                   "fc_dec<true,false,4,4,2,false,true,4> (FC1, bf16, 16-row tiles, group schedule)" if args.m > 4
+                   else "fc_dec<true,false,2,4,2,true,true,4> (FC1, bf16, one route per tile, group schedule)"),
+        "kernel_us": round(fc1_us, 2),
         "alg_bytes_per_launch": int(r["fc1_bytes"])}
     if ceil:
         line["roofline"]["measured_peak"] = ceil["hbm_read_nt_gbs"]

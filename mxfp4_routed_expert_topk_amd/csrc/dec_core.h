@@ -54,6 +54,12 @@ struct AFrag<true> { uint4 lo, hi; uint32_t scale; };  // 32 E4M3 + E8M0 of grou
 // block moved four times the scale bytes through the load path); measured
 // FC1 548 -> 515 us and FC2 287 -> 278 us at 128 tokens.
 //
+// Two K ranges in one wave (GRP only): with `first` given, the wave runs
+// [lo, hi) as one loop but parks the sum of [lo, split) in `first` when the
+// loop reaches split and restarts acc from zero, so each range keeps the sum
+// it has when a wave of its own computes it (split is a group boundary, met
+// at the start of a turn).
+//
 // ALDS (bf16 only): every lane's A row is the same row (one route per tile).
 // Loaded per lane, each column block took four 1 KB load instructions for
 // 256 distinct bytes; instead the wave copies its K range of the row to its
@@ -62,7 +68,8 @@ struct AFrag<true> { uint4 lo, hi; uint32_t scale; };  // 32 E4M3 + E8M0 of grou
 // reads).  Only this wave touches its region, so no barrier is needed.
 template <bool FC1, bool MX, int NBW, int P, bool PIPE = false, bool ALDS = false, bool GRP = false>
 __device__ __forceinline__ void dec_kloop(const FcArgs& a, int e, int nb0, long long arow, int lo, int hi,
-                                          f32x4_t (&acc)[NBW], uint8_t* alds = nullptr) {
+                                          f32x4_t (&acc)[NBW], uint8_t* alds = nullptr, int split = 0,
+                                          f32x4_t* first = nullptr) {
   static_assert(!(ALDS && MX), "the staged row is bf16");
   static_assert(!GRP || P == 2, "the group schedule keeps two column blocks in flight");
   const int lane = threadIdx.x & (kWave - 1);
@@ -75,7 +82,10 @@ __device__ __forceinline__ void dec_kloop(const FcArgs& a, int e, int nb0, long 
   const int n = hi - lo;
 
 #pragma unroll
-  for (int j = 0; j < NBW; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < NBW; ++j) {
+    acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    if (first) first[j] = acc[j];
+  }
 
   uint4 Wr[P][NBW];
   uint32_t Sr[P][NBW];
@@ -207,6 +217,13 @@ __device__ __forceinline__ void dec_kloop(const FcArgs& a, int e, int nb0, long 
       // left free, the scheduler moved the next group's scale loads to the
       // end of the turn, right before their first use)
       for (int it = 0; it < n; it += 4) {
+        if (first && lo + it == split) {
+#pragma unroll
+          for (int j = 0; j < NBW; ++j) {
+            first[j] = acc[j];
+            acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          }
+        }
         uint32_t cur[NBW];
 #pragma unroll
         for (int j = 0; j < NBW; ++j) cur[j] = Sr[0][j];

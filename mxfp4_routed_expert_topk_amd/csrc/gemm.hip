@@ -1,10 +1,13 @@
 // Grouped FC1 / FC2 over MXFP4 expert weights, 16-row tiles (decode sizes).
 //
-// Work item = (16-row tile, group of NBW 16-row weight blocks).  A workgroup
-// of KSPLIT waves splits K into KSPLIT contiguous ranges (a function of K
-// only, so the fp32 summation order of a row does not depend on the batch);
-// each wave runs the shared K loop (dec_core.h) over its range, and the
-// KSPLIT partial sums are added through LDS in wave order 0, 1, ..., KSPLIT-1.
+// Work item = (16-row tile, group of NBW 16-row weight blocks).  K is split
+// into KSPLIT contiguous ranges (a function of K only, so the fp32 summation
+// order of a row does not depend on the batch), and the KSPLIT partial sums
+// are added in range order 0, 1, ..., KSPLIT-1.  A workgroup has WAVES waves:
+// with WAVES = KSPLIT each wave runs the shared K loop (dec_core.h) over one
+// range and the sums meet in LDS; with WAVES = KSPLIT / 2 a wave runs two
+// adjacent ranges as one loop with one parked partial sum (the same bits);
+// with one wave the sums are added in registers.
 //
 // Tiles come from the route stage (the rows of one expert, 16 at a time;
 // tiles past the device-side tile count exit at once) or, for the smallest
@@ -25,9 +28,12 @@
 namespace moe {
 namespace {
 
-template <bool FC1, bool MX, int NBW, int KSPLIT, int P, bool PER_ROUTE, bool GRP>
-__global__ __launch_bounds__(kWave * KSPLIT) void fc_dec(FcArgs a) {
+template <bool FC1, bool MX, int NBW, int KSPLIT, int P, bool PER_ROUTE, bool GRP, int WAVES = KSPLIT>
+__global__ __launch_bounds__(kWave * WAVES) void fc_dec(FcArgs a) {
   static_assert(!FC1 || NBW % 2 == 0, "FC1 groups hold gate/up pairs");
+  constexpr int R = KSPLIT / WAVES;   // K ranges per wave
+  static_assert(R * WAVES == KSPLIT && R <= 2 && (R == 1 || (GRP && !PER_ROUTE)),
+                "two ranges per wave run on the group schedule");
   const int tile = blockIdx.y;
   int e, row0, rows;
   if constexpr (PER_ROUTE) {                 // tile = route f, one row
@@ -53,9 +59,16 @@ __global__ __launch_bounds__(kWave * KSPLIT) void fc_dec(FcArgs a) {
 
   const int nb0 = blockIdx.x * NBW;
   int lo, hi;
-  dec_krange<KSPLIT>(a.mat.kb, wave, &lo, &hi);
+  dec_krange<KSPLIT>(a.mat.kb, wave * R, &lo, &hi);
   f32x4_t acc[NBW];
-  if constexpr (PER_ROUTE && !MX) {
+  f32x4_t first[NBW];   // R = 2: the sum of the wave's first range
+  if constexpr (R == 2) {
+    int lo1, hi1;
+    dec_krange<KSPLIT>(a.mat.kb, wave * R + 1, &lo1, &hi1);
+    const int split = hi;
+    hi = max(hi, hi1);
+    dec_kloop<FC1, MX, NBW, P, !FC1, false, GRP>(a, e, nb0, arow, lo, hi, acc, nullptr, split, first);
+  } else if constexpr (PER_ROUTE && !MX) {
     // one token row per tile: each wave stages its K range of it in its own
     // share of the dynamic LDS (launch_dec sizes it: KSPLIT ranges); measured
     // FC1 21.4 -> 19.0 us at one token, 58.5 -> 51.3 us at four
@@ -66,25 +79,41 @@ __global__ __launch_bounds__(kWave * KSPLIT) void fc_dec(FcArgs a) {
     dec_kloop<FC1, MX, NBW, P, !FC1, false, GRP>(a, e, nb0, arow, lo, hi, acc);
   }
 
-  // every wave parks its partial sums; the epilogue adds them in wave order
-  __shared__ float red[KSPLIT][NBW][4][kWave];
-#pragma unroll
-  for (int j = 0; j < NBW; ++j)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) red[wave][j][i][lane] = acc[j][i];
-  __syncthreads();
-
+  // the partial sums of the K ranges, added in range order: in registers
+  // with one wave, else parked in LDS by range
   constexpr int NEPI = FC1 ? NBW / 2 : NBW;   // output column blocks of the group
-  for (int c = wave; c < NEPI; c += KSPLIT) {
+  __shared__ float red[WAVES == 1 ? 1 : KSPLIT][NBW][4][kWave];
+  if constexpr (WAVES > 1) {
+#pragma unroll
+    for (int j = 0; j < NBW; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if constexpr (R == 2) red[wave * R][j][i][lane] = first[j][i];
+        red[wave * R + R - 1][j][i][lane] = acc[j][i];
+      }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int c = WAVES == 1 ? 0 : wave; c < NEPI; c += WAVES) {
     float v0[4], v1[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int j0 = FC1 ? 2 * c : c;
-      float s0 = red[0][j0][i][lane], s1 = FC1 ? red[0][j0 + 1][i][lane] : 0.f;
+      float s0, s1 = 0.f;
+      if constexpr (WAVES == 1 && R == 2) {
+        s0 = first[j0][i] + acc[j0][i];
+        if (FC1) s1 = first[j0 + 1][i] + acc[j0 + 1][i];
+      } else if constexpr (WAVES == 1) {
+        s0 = acc[j0][i];
+        if (FC1) s1 = acc[j0 + 1][i];
+      } else {
+        s0 = red[0][j0][i][lane];
+        if (FC1) s1 = red[0][j0 + 1][i][lane];
 #pragma unroll
-      for (int w = 1; w < KSPLIT; ++w) {
-        s0 += red[w][j0][i][lane];
-        if (FC1) s1 += red[w][j0 + 1][i][lane];
+        for (int w = 1; w < KSPLIT; ++w) {
+          s0 += red[w][j0][i][lane];
+          if (FC1) s1 += red[w][j0 + 1][i][lane];
+        }
       }
       v0[i] = s0;
       v1[i] = s1;
@@ -107,7 +136,8 @@ __global__ __launch_bounds__(kWave * KSPLIT) void fc_dec(FcArgs a) {
   }
 }
 
-template <bool FC1, bool MX, int NBW, int KSPLIT, int P, bool PER_ROUTE>
+// R = K ranges per wave (the group schedule only; 1 without it).
+template <bool FC1, bool MX, int NBW, int KSPLIT, int P, bool PER_ROUTE, int R>
 hipError_t launch_dec(const FcArgs& a, int tiles_max, hipStream_t stream) {
   const dim3 grid(a.mat.nb / NBW, tiles_max);
   const size_t lds = PER_ROUTE && !MX ? (size_t)KSPLIT * dec_krange_max(a.mat.kb, KSPLIT) * kTileK * 2 : 0;
@@ -115,32 +145,42 @@ hipError_t launch_dec(const FcArgs& a, int tiles_max, hipStream_t stream) {
   // four column blocks; measured 6 % faster FC1 and 3 % faster FC2 at 128
   // tokens, 2-7 % faster layers from 1 to 128 tokens)
   if (a.mat.kb % 4 == 0)
-    hipLaunchKernelGGL((fc_dec<FC1, MX, NBW, KSPLIT, P, PER_ROUTE, true>), grid, dim3(kWave * KSPLIT), lds, stream, a);
+    hipLaunchKernelGGL((fc_dec<FC1, MX, NBW, KSPLIT, P, PER_ROUTE, true, KSPLIT / R>), grid,
+                       dim3(kWave * (KSPLIT / R)), lds, stream, a);
   else
-    hipLaunchKernelGGL((fc_dec<FC1, MX, NBW, KSPLIT, P, PER_ROUTE, false>), grid, dim3(kWave * KSPLIT), lds, stream, a);
+    hipLaunchKernelGGL((fc_dec<FC1, MX, NBW, KSPLIT, P, PER_ROUTE, false>), grid, dim3(kWave * KSPLIT), lds, stream,
+                       a);
   return hipGetLastError();
 }
 
 // The K split is fixed per matrix (it sets the fp32 summation order); the
-// row-block group width and the load depth only change the schedule.
+// row-block group width, the load depth and the ranges per wave only change
+// the schedule.
 constexpr int kSmallTokens = 4;
 
-template <bool FC1, bool MX, int NBW, int P, bool PER_ROUTE = false>
+template <bool FC1, bool MX, int NBW, int P, bool PER_ROUTE = false, int R = 1>
 hipError_t launch_sched(const FcArgs& a, int tiles_max, hipStream_t stream) {
-  if (dec_ksplit(a.mat.kb) == 4) return launch_dec<FC1, MX, NBW, 4, P, PER_ROUTE>(a, tiles_max, stream);
-  return launch_dec<FC1, MX, NBW, 2, P, PER_ROUTE>(a, tiles_max, stream);
+  if (dec_ksplit(a.mat.kb) == 4) return launch_dec<FC1, MX, NBW, 4, P, PER_ROUTE, R>(a, tiles_max, stream);
+  return launch_dec<FC1, MX, NBW, 2, P, PER_ROUTE, R>(a, tiles_max, stream);
 }
 
 // Schedules (every row-block count here is a multiple of 8: H, I multiples of
 // 128).  Up to 4 tokens: two row blocks per workgroup, two column blocks
-// loaded ahead; larger batches: four row blocks (measured 9-10 % faster than
-// two from 8 to 16 tokens; eight FC1 row blocks, or three column blocks ahead,
-// were slower there; with the group schedule four FC2 row blocks also beat
-// eight by 3-4 % at 64 and 128 tokens).
+// loaded ahead, one K range per wave (the most waves for the fewest tiles);
+// larger batches: four row blocks (measured 9-10 % faster than two from 8 to
+// 16 tokens; eight FC1 row blocks, or three column blocks ahead, were slower
+// there; with the group schedule four FC2 row blocks also beat eight by 3-4 %
+// at 64 and 128 tokens).  Two K ranges per wave: FC2 (intermediate 2048: one
+// wave per workgroup) 286 -> 271 us at 128 tokens, 51 -> 50 us at 8; FC1
+// (hidden 7168: two waves) about 1 % faster from 64 tokens, 3 % slower at 8,
+// where fewer waves leave the chip short of loads in flight.
+constexpr int kWideFc1Tokens = 32;
+
 template <bool FC1, bool MX>
 hipError_t launch_fc(const FcArgs& a, int tiles_max, int tokens, hipStream_t stream) {
   if (tokens <= kSmallTokens) return launch_sched<FC1, MX, 2, 2>(a, tiles_max, stream);
-  return launch_sched<FC1, MX, 4, 2>(a, tiles_max, stream);
+  if (FC1 && tokens < kWideFc1Tokens) return launch_sched<FC1, MX, 4, 2>(a, tiles_max, stream);
+  return launch_sched<FC1, MX, 4, 2, false, 2>(a, tiles_max, stream);
 }
 
 }  // namespace

@@ -493,6 +493,40 @@ def test_small_and_large_decode_schedules_give_the_same_bits(act):
     assert not G.bf16_bits(out).any() and not acc.cpu().numpy().view(np.uint32).any()
 
 
+@pytest.mark.gpu
+@pytest.mark.parametrize("act", ["bf16", "mxfp8"])
+def test_two_k_ranges_per_wave_give_the_same_bits(act):
+    """From 32 tokens the decode FC1 waves run two K ranges each (FC2 from 5
+    tokens), parking the first range's sum: hidden 5120 gives FC1 40 column
+    blocks in four ranges of 12, 12, 8, 8 (one wave takes 0-24 with a split at
+    12, the other 24-40 with a split at 32), intermediate 1536 gives FC2 12
+    blocks in ranges of 8 and 4 (one wave, split at 8).  The rows of 40
+    tokens (two ranges per FC1 and FC2 wave), 16 (one per FC1 wave), 4 (the
+    per-route path for bf16) and 1 agree bit for bit, and three of the rows
+    match the oracle."""
+    case = W.make_case("ranges", W.LayerShape(40, 5120, 1536, 48, 60, 8), 91, routing="uniform",
+                       invalid_frac=0.1, act=act)
+    say(f"two K ranges per wave ({act}): 40 tokens, hidden 5120, intermediate 1536, 48 experts")
+    plan, _ = G.make_plan(case)
+    x = G.to_dev(case.hidden_bits).view(torch.bfloat16)
+    ids = G.to_dev(case.topk_ids)
+    wts = G.to_dev(case.topk_weights)
+
+    def run(n):
+        acc = torch.full((n, 5120), float("nan"), device=x.device)
+        out = torch.full((n, 5120), float("nan"), dtype=torch.bfloat16, device=x.device)
+        plan.forward(x, ids, wts, out=out, acc=acc, num_tokens=n)
+        torch.cuda.synchronize()
+        return out, acc
+
+    out40, acc40 = run(40)
+    check_layer(case, out40, acc40, tokens=[0, 21, 39], plan=plan)   # before h is overwritten
+    for n in (16, 4, 1):
+        out_n, acc_n = run(n)
+        np.testing.assert_array_equal(G.bf16_bits(out_n), G.bf16_bits(out40)[:n])
+        np.testing.assert_array_equal(acc_n.cpu().numpy().view(np.uint32), acc40.cpu().numpy()[:n].view(np.uint32))
+
+
 def test_prefill_workspace_with_stale_bytes_gives_the_same_bits():
     """The bf16 prefill kernels take their work items from counters in the
     workspace, which the route stage zeroes in the stream every forward: a
