@@ -136,11 +136,21 @@ __global__ __launch_bounds__(kWave * WAVES) void fc_dec(FcArgs a) {
   }
 }
 
+// CAP: single-wave workgroups reserve a sixth of the CU's 160 KB of LDS
+// (unused: an occupancy cap) so that at most six share a CU.  Measured for
+// FC2 at intermediate 2048, same box, against eight per CU (the register
+// limit): 270 -> 261 us at 128 tokens, 210 -> 206 us at 64, equal at 16 and
+// slightly slower at 8; seven per CU gained half as much, five the same as
+// six, four nothing.
+constexpr int kOneWaveWgPerCu = 6;
+constexpr size_t kOneWaveWgLds = (160 * 1024 / kOneWaveWgPerCu) & ~(size_t)511;
+
 // R = K ranges per wave (the group schedule only; 1 without it).
-template <bool FC1, bool MX, int NBW, int KSPLIT, int P, bool PER_ROUTE, int R>
+template <bool FC1, bool MX, int NBW, int KSPLIT, int P, bool PER_ROUTE, int R, bool CAP = false>
 hipError_t launch_dec(const FcArgs& a, int tiles_max, hipStream_t stream) {
   const dim3 grid(a.mat.nb / NBW, tiles_max);
-  const size_t lds = PER_ROUTE && !MX ? (size_t)KSPLIT * dec_krange_max(a.mat.kb, KSPLIT) * kTileK * 2 : 0;
+  const size_t lds = PER_ROUTE && !MX ? (size_t)KSPLIT * dec_krange_max(a.mat.kb, KSPLIT) * kTileK * 2
+                     : CAP && KSPLIT / R == 1 && a.mat.kb % 4 == 0 ? kOneWaveWgLds : 0;
   // whole scale groups per K range: the group schedule (one scale load per
   // four column blocks; measured 6 % faster FC1 and 3 % faster FC2 at 128
   // tokens, 2-7 % faster layers from 1 to 128 tokens)
@@ -158,10 +168,10 @@ hipError_t launch_dec(const FcArgs& a, int tiles_max, hipStream_t stream) {
 // the schedule.
 constexpr int kSmallTokens = 4;
 
-template <bool FC1, bool MX, int NBW, int P, bool PER_ROUTE = false, int R = 1>
+template <bool FC1, bool MX, int NBW, int P, bool PER_ROUTE = false, int R = 1, bool CAP = false>
 hipError_t launch_sched(const FcArgs& a, int tiles_max, hipStream_t stream) {
-  if (dec_ksplit(a.mat.kb) == 4) return launch_dec<FC1, MX, NBW, 4, P, PER_ROUTE, R>(a, tiles_max, stream);
-  return launch_dec<FC1, MX, NBW, 2, P, PER_ROUTE, R>(a, tiles_max, stream);
+  if (dec_ksplit(a.mat.kb) == 4) return launch_dec<FC1, MX, NBW, 4, P, PER_ROUTE, R, CAP>(a, tiles_max, stream);
+  return launch_dec<FC1, MX, NBW, 2, P, PER_ROUTE, R, CAP>(a, tiles_max, stream);
 }
 
 // Schedules (every row-block count here is a multiple of 8: H, I multiples of
@@ -173,14 +183,18 @@ hipError_t launch_sched(const FcArgs& a, int tiles_max, hipStream_t stream) {
 // at 64 and 128 tokens).  Two K ranges per wave: FC2 (intermediate 2048: one
 // wave per workgroup) 286 -> 271 us at 128 tokens, 51 -> 50 us at 8; FC1
 // (hidden 7168: two waves) about 1 % faster from 64 tokens, 3 % slower at 8,
-// where fewer waves leave the chip short of loads in flight.
-constexpr int kWideFc1Tokens = 32;
+// where fewer waves leave the chip short of loads in flight.  The same
+// threshold turns on the single-wave workgroup cap (CAP above).
+constexpr int kWideTokens = 32;
 
 template <bool FC1, bool MX>
 hipError_t launch_fc(const FcArgs& a, int tiles_max, int tokens, hipStream_t stream) {
   if (tokens <= kSmallTokens) return launch_sched<FC1, MX, 2, 2>(a, tiles_max, stream);
-  if (FC1 && tokens < kWideFc1Tokens) return launch_sched<FC1, MX, 4, 2>(a, tiles_max, stream);
-  return launch_sched<FC1, MX, 4, 2, false, 2>(a, tiles_max, stream);
+  if (tokens < kWideTokens) {
+    if (FC1) return launch_sched<FC1, MX, 4, 2>(a, tiles_max, stream);
+    return launch_sched<FC1, MX, 4, 2, false, 2>(a, tiles_max, stream);
+  }
+  return launch_sched<FC1, MX, 4, 2, false, 2, true>(a, tiles_max, stream);
 }
 
 }  // namespace
