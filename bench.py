@@ -57,7 +57,7 @@ FP8_PEAK_TFLOPS = 5000.0       # dense fp8 MFMA
 METRIC = "MoE layer tokens/s + % HBM roofline (decode M≤128) / % MFMA peak (prefill)"
 STAGES = ("route", "fc1", "fc2", "combine")
 FLUSH_BYTES = 1 << 30
-SETTLE_S = 0.05                # minimum untimed warm-up of the extra workloads (clock ramp after host work)
+SETTLE_S = 0.05                # minimum untimed warm-up of every workload (clock ramp after host work)
 FLOOR_BYTES = 2 << 30          # source of the stream-floor probe: revisited only after 2 GiB of other reads
 CONTEXT = {
     "pages_full_model_decode_step_ms": {"fused_megamoe": 43.3, "nccl_fixed_chain": 54.6},
@@ -264,8 +264,9 @@ class Batches:
         pairs warm and cold, stage events (per-kernel times on the launch
         stream), graph replay, and optionally the one-launch forward.  With
         `settle_s`, the untimed warm-up goes on past `warmup` steps until that
-        many seconds have passed (the extra workloads: each starts after
-        seconds of host-side input generation, with the GPU's clocks down)."""
+        many seconds have passed (every workload starts after host-side work:
+        input generation, or the ceiling probes, with the GPU's clocks not yet
+        at the layer's steady state)."""
         import torch
         t0 = time.time()
         j = 0
@@ -298,7 +299,7 @@ class Batches:
         self.plan.set_stage_events(None)
         stage = np.array([[e[i].elapsed_time(e[i + 1]) for i in range(4)] for e in evs])  # ms
         alg = np.array([self.per_step(warmup + j) for j in range(steps)])
-        return {"ms_per_step": ms, "warm_ms": warm, "cold_ms": cold,
+        return {"ms_per_step": ms, "warmup_steps_run": warmup, "warm_ms": warm, "cold_ms": cold,
                 "ms_per_step_with_events": float(stage.sum(axis=1).mean()),
                 "stage_ms": stage.mean(axis=0), "fc1_ms": stage[:, 1],
                 "layer_bytes": alg[:, 0].mean(), "fc1_bytes": alg[:, 1].mean(), "flops": alg[:, 2].mean(),
@@ -571,7 +572,8 @@ def router_timings(reps=200):
 
 def base_line(args, r, summ, config):
     return {"metric": METRIC, "value": summ["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
-            "warmup": args.warmup, "ms_per_step": round(r["ms_per_step"], 5), "higher_is_better": True,
+            "warmup": args.warmup, "warmup_steps_run": r["warmup_steps_run"],
+            "ms_per_step": round(r["ms_per_step"], 5), "higher_is_better": True,
             "scaling": "weak", "vs_baseline": None, "data": "synthetic", "config": config, "layer": summ}
 
 
@@ -583,7 +585,7 @@ def prefill_line(args, measured_ceilings):
     pl, _ = build_plan(cid, case.shape.tokens)
     b = Batches.config(pl, cid, None, 2)
     ceil = measured_ceilings()
-    r = b.run(args.steps, args.warmup)
+    r = b.run(args.steps, args.warmup, SETTLE_S)
     summ = b.summary(r, ceil)
     mx = case.act == "mxfp8"
     s = case.shape
@@ -671,7 +673,7 @@ def main():
     plan, _ = build_plan(1, max(max(W.DECODE_M), args.m))
     head_b = Batches.config(plan, 1, args.m, args.sets)
     ceil = measured_ceilings()
-    r = head_b.run(args.steps, args.warmup)
+    r = head_b.run(args.steps, args.warmup, SETTLE_S)
     head = head_b.summary(r, ceil)
     log(f"decode M={args.m}: {head}")
     fc1_us = float(np.mean(r["fc1_ms"])) * 1e3
