@@ -136,6 +136,7 @@ __device__ __forceinline__ void ring_pass(F& f, int s0, int n) {
   }
 }
 
+// NT: the weight loads carry the non-temporal hint.
 // The K loop with the weights in registers: only the activation rows, which
 // the four waves share, go through LDS (a ring of D + 1 stages); each wave
 // loads its own weight chunks -- the 16 code bytes a lane multiplies in each
@@ -146,7 +147,7 @@ __device__ __forceinline__ void ring_pass(F& f, int s0, int n) {
 // outside their buffer resource, which return zeros without a memory request),
 // so the wait before each stage counts them exactly and the compiler never
 // waits at the MFMAs for weights still in flight.
-template <class C, int LIVE, int D>
+template <class C, int LIVE, int D, bool NT>
 __device__ __forceinline__ void k_loop_r(uint8_t* smem, const uint8_t* const (&srcA)[C::nA],
                                          __amdgpu_buffer_rsrc_t rcode, __amdgpu_buffer_rsrc_t rscale,
                                          const uint32_t (&coff)[2], const uint32_t (&soff)[2], int S, int wave,
@@ -190,7 +191,7 @@ __device__ __forceinline__ void k_loop_r(uint8_t* smem, const uint8_t* const (&s
       } else if (c < NA + NJ) {
         const int nj = c - NA;
         bc[slot][nj] = __builtin_amdgcn_raw_buffer_load_b128(rcode, real ? coff[nj] : kPastEnd,
-                                                             real ? st * kHalfTile : 0, 0);
+                                                             real ? st * kHalfTile : 0, NT ? 2 : 0);
       } else {
         const int hf = (c - NA - NJ) / NJ, nj = (c - NA - NJ) % NJ;
         sraw[hf][nj] = __builtin_amdgcn_raw_buffer_load_b32(rscale, real ? soff[nj] : kPastEnd,
@@ -448,11 +449,27 @@ __device__ __noinline__ void fc_pre_item(const FcArgs& a, uint8_t* smem, int sli
 
   const int S = 2 * M.kb;    // stages
   static_assert(MI == 4, "128-row tiles");
-  switch (live) {
-    case 1: k_loop_r<C, 1, depth_for<1>()>(smem, srcA, rcode, rscale, coff, soff, S, wave, lane, acc); break;
-    case 2: k_loop_r<C, 2, depth_for<2>()>(smem, srcA, rcode, rscale, coff, soff, S, wave, lane, acc); break;
-    case 3: k_loop_r<C, 3, depth_for<3>()>(smem, srcA, rcode, rscale, coff, soff, S, wave, lane, acc); break;
-    default: k_loop_r<C, 4, depth_for<4>()>(smem, srcA, rcode, rscale, coff, soff, S, wave, lane, acc); break;
+  // Cache policy of the weight loads: an expert with one tile has its weights
+  // read by this item alone, so they stream non-temporally; an expert with
+  // more tiles (Zipf-popular ones) is read again by its other tiles' items,
+  // so they stay cacheable (measured: non-temporal everywhere 2.5 % faster on
+  // the 1536-token uniform layer and 2.6 % slower on the 4096-token Zipf one;
+  // chosen per tile, 2.2 % and 1.2 % faster than plain loads everywhere).
+  const bool single = uni(a.offsets[e + 1] - a.offsets[e]) <= BM;
+  if (single) {
+    switch (live) {
+      case 1: k_loop_r<C, 1, depth_for<1>(), true>(smem, srcA, rcode, rscale, coff, soff, S, wave, lane, acc); break;
+      case 2: k_loop_r<C, 2, depth_for<2>(), true>(smem, srcA, rcode, rscale, coff, soff, S, wave, lane, acc); break;
+      case 3: k_loop_r<C, 3, depth_for<3>(), true>(smem, srcA, rcode, rscale, coff, soff, S, wave, lane, acc); break;
+      default: k_loop_r<C, 4, depth_for<4>(), true>(smem, srcA, rcode, rscale, coff, soff, S, wave, lane, acc); break;
+    }
+  } else {
+    switch (live) {
+      case 1: k_loop_r<C, 1, depth_for<1>(), false>(smem, srcA, rcode, rscale, coff, soff, S, wave, lane, acc); break;
+      case 2: k_loop_r<C, 2, depth_for<2>(), false>(smem, srcA, rcode, rscale, coff, soff, S, wave, lane, acc); break;
+      case 3: k_loop_r<C, 3, depth_for<3>(), false>(smem, srcA, rcode, rscale, coff, soff, S, wave, lane, acc); break;
+      default: k_loop_r<C, 4, depth_for<4>(), false>(smem, srcA, rcode, rscale, coff, soff, S, wave, lane, acc); break;
+    }
   }
   const int next = threadIdx.x == 0 ? atomicAdd(counter, 1) : 0;
   const int n32 = lane & 31, h = lane >> 5;
