@@ -140,22 +140,38 @@ __global__ __launch_bounds__(kThreads) void route_count(const int32_t* ids, int 
   if (t < E) blockcounts[(size_t)blockIdx.x * E + t] = s_cnt[t];
 }
 
-// Chunked: totals, offsets, tiles; blockcounts become each chunk's first row per expert.
+// Chunked: totals, offsets, tiles; blockcounts become each chunk's first row
+// per expert.  Thread e walks expert e's counts down the chunks eight at a
+// time, the eight loads issued together (one load and, in the second pass, one
+// store after the other waited for each load in turn: 15 us at 32 chunks).
+constexpr int kScanBatch = 8;
+
 __global__ __launch_bounds__(kThreads) void route_scan(int E, int nblk, int bm, RouteOut o) {
   __shared__ int tmp[kWaves];
   if (o.sched != nullptr && threadIdx.x < kSchedCounters) o.sched[threadIdx.x] = 0;
   const int e = threadIdx.x;
   int total = 0;
   if (e < E)
-    for (int b = 0; b < nblk; ++b) total += o.blockcounts[(size_t)b * E + e];
+    for (int b0 = 0; b0 < nblk; b0 += kScanBatch) {
+      int c[kScanBatch];
+#pragma unroll
+      for (int j = 0; j < kScanBatch; ++j) c[j] = b0 + j < nblk ? o.blockcounts[(size_t)(b0 + j) * E + e] : 0;
+#pragma unroll
+      for (int j = 0; j < kScanBatch; ++j) total += c[j];
+    }
   finish_counts(e, total, E, bm, tmp, o, nullptr);
   __syncthreads();
   if (e < E) {
     int run = o.offsets[e];
-    for (int b = 0; b < nblk; ++b) {
-      const int c = o.blockcounts[(size_t)b * E + e];
-      o.blockcounts[(size_t)b * E + e] = run;
-      run += c;
+    for (int b0 = 0; b0 < nblk; b0 += kScanBatch) {
+      int c[kScanBatch];
+#pragma unroll
+      for (int j = 0; j < kScanBatch; ++j) c[j] = b0 + j < nblk ? o.blockcounts[(size_t)(b0 + j) * E + e] : 0;
+#pragma unroll
+      for (int j = 0; j < kScanBatch; ++j) {
+        if (b0 + j < nblk) o.blockcounts[(size_t)(b0 + j) * E + e] = run;
+        run += c[j];
+      }
     }
   }
 }
