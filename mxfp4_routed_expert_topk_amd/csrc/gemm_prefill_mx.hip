@@ -9,8 +9,8 @@
 // holds 23.4 MB of codes and scales at hidden 7168 / intermediate 2048, while
 // its ~85 routed rows of E4M3 activations hold 0.6 MB), so one tile covers
 // every row an expert has in a balanced batch and each weight byte is read
-// once.  A workgroup of WV waves (eight where the matrix's rows come in 512s,
-// one workgroup per CU; else four, two per CU) runs one stage per
+// once.  A workgroup of WV waves (eight for FC1 where the matrix's rows come
+// in 512s, one workgroup per CU; else four, two per CU) runs one stage per
 // 128-K column block, loading stage st + kDepth while stage st multiplies:
 //  * weights: the repacked 1 KB tile is already the MFMA's B operand (lane l
 //    holds the 32 codes of row l%16, K group l/16), so each wave loads its
@@ -384,12 +384,15 @@ hipError_t launch_waves(const FcArgs& a, int tiles_max, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Eight waves (512 columns) where the matrix's rows allow it: the staged
-// activation rows then serve twice the columns (measured 4 % faster in FC1 at
-// 4096 tokens than two four-wave workgroups per CU); else four.
+// FC1: eight waves (512 columns) where the matrix's rows allow it: the staged
+// activation rows then serve twice the columns (measured 4 % faster at 4096
+// tokens than two four-wave workgroups per CU); else four.  FC2 (K = I: 16
+// stages at intermediate 2048, so the ring's fill and the epilogue weigh
+// more): four, two workgroups per CU, one filling the gaps of the other
+// (measured 676 -> 642 us at 4096 tokens and 384 experts).
 template <bool FC1>
 hipError_t launch(const FcArgs& a, int tiles_max, hipStream_t stream) {
-  if (a.mat.nb % (8 * kNBW) == 0) return launch_waves<FC1, 8>(a, tiles_max, stream);
+  if (FC1 && a.mat.nb % (8 * kNBW) == 0) return launch_waves<FC1, 8>(a, tiles_max, stream);
   return launch_waves<FC1, 4>(a, tiles_max, stream);
 }
 
