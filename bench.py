@@ -440,31 +440,36 @@ class Batches:
         return start.elapsed_time(end) / steps
 
     def run_graph(self, steps, warmup):
-        """The same steps replayed from one captured hipGraph per input set (the
-        forward enqueues only kernels, so it captures as is): the per-launch
-        host and queue gaps drop out, as in a serving loop."""
+        """The same steps replayed from one captured hipGraph that holds a
+        forward for every input set in turn (the forward enqueues only kernels,
+        so it captures as is), as a serving loop would capture a whole
+        model's layers: the per-launch host and queue gaps drop out, and one
+        graph launch covers several forwards (at one forward per graph the
+        graph launch itself costs more than a small batch's two kernel
+        launches).  Replayed until at least `steps` forwards have run;
+        microseconds per forward."""
         import torch
-        graphs = []
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
+        g = torch.cuda.CUDAGraph()
         with torch.cuda.stream(side):
-            for x, ids, wts in self.inputs:
-                g = torch.cuda.CUDAGraph()
-                with torch.cuda.graph(g, stream=side):
+            with torch.cuda.graph(g, stream=side):
+                for x, ids, wts in self.inputs:
                     self.plan.forward(x, ids, wts, out=self.out, acc=self.acc)
-                graphs.append(g)
         torch.cuda.current_stream().wait_stream(side)
-        for j in range(warmup):
-            graphs[j % len(graphs)].replay()
+        per = len(self.inputs)
+        for _ in range(max(1, -(-warmup // per))):
+            g.replay()
+        reps = max(1, -(-steps // per))
         start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         start.record()
-        for j in range(steps):
-            graphs[(warmup + j) % len(graphs)].replay()
+        for _ in range(reps):
+            g.replay()
         end.record()
         torch.cuda.synchronize()
-        del graphs
-        return start.elapsed_time(end) / steps
+        del g
+        return start.elapsed_time(end) / (reps * per)
 
     def summary(self, r, ceil=None):
         ms = r["ms_per_step"]
