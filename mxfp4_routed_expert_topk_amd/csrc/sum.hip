@@ -22,12 +22,12 @@
 namespace moe {
 namespace {
 
-// Eight waves per workgroup, two column blocks loaded ahead; 32 output
+// Eight waves per workgroup, two column blocks loaded ahead; 16 output
 // columns per workgroup for a single token, 64 above (measured at hidden
 // 7168, intermediate 2048, top-8: 30.2 / 90.8 us per layer at 1 / 4 tokens,
 // against 34.9 / 99.7 us for the route + FC1 + FC2 + combine chain; wider
 // workgroups lost at one token, narrower ones at four, sixteen waves and
-// deeper loads lost everywhere).
+// deeper loads lost everywhere; at one token 16 columns beat 32 by 0.4 us).
 constexpr int kSumWaves = 8;
 constexpr int kSumP = 2;
 
@@ -59,7 +59,7 @@ __global__ __launch_bounds__(kWave * kSumWaves) void fc2_sum(FcArgs a, const flo
     // one token: the unit's h row segment staged in LDS (1-token layer 13.6 ->
     // 13.2 us in this kernel); at four tokens the per-lane loads measured
     // 0.7 us faster
-    dec_kloop<false, false, NBW, kSumP, (NBW > 2), (NBW == 2), GRP>(a, e, nb0, (long long)(f0 + s), lo, hi, acc,
+    dec_kloop<false, false, NBW, kSumP, (NBW > 2), (NBW <= 2), GRP>(a, e, nb0, (long long)(f0 + s), lo, hi, acc,
                                                                     row_lds + wave * per * (kTileK * 2));
     if (lane < kTileN)                                  // D row 0: lanes 0..15 hold a block's 16 columns
 #pragma unroll
@@ -87,7 +87,7 @@ hipError_t launch_sum(const FcArgs& a, const float* weights, int32_t T, int32_t 
                       hipStream_t stream) {
   const dim3 grid(a.mat.nb / NBW, T), block(kWave * kSumWaves);
   const int ks = dec_ksplit(a.mat.kb);
-  const size_t lds = NBW == 2 ? (size_t)kSumWaves * dec_krange_max(a.mat.kb, ks) * kTileK * 2 : 0;
+  const size_t lds = NBW <= 2 ? (size_t)kSumWaves * dec_krange_max(a.mat.kb, ks) * kTileK * 2 : 0;
   const bool grp = a.mat.kb % 4 == 0;   // whole scale groups per K range
   if (ks == 4) {
     if (grp) hipLaunchKernelGGL((fc2_sum<4, NBW, true>), grid, block, lds, stream, a, weights, H, acc, out);
@@ -104,7 +104,7 @@ hipError_t launch_sum(const FcArgs& a, const float* weights, int32_t T, int32_t 
 hipError_t launch_fc2_sum_per_route(const FcArgs& a, const float* weights, int32_t T, int32_t H, float* acc,
                                     uint16_t* out, hipStream_t stream) {
   // every row-block count is a multiple of 8 (H a multiple of 128)
-  if (T == 1) return launch_sum<2>(a, weights, T, H, acc, out, stream);
+  if (T == 1) return launch_sum<1>(a, weights, T, H, acc, out, stream);
   return launch_sum<4>(a, weights, T, H, acc, out, stream);
 }
 
