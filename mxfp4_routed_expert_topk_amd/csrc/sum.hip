@@ -22,12 +22,18 @@
 namespace moe {
 namespace {
 
-// Eight waves per workgroup, two column blocks loaded ahead; 16 output
-// columns per workgroup for a single token, 64 above (measured at hidden
-// 7168, intermediate 2048, top-8: 30.2 / 90.8 us per layer at 1 / 4 tokens,
-// against 34.9 / 99.7 us for the route + FC1 + FC2 + combine chain; wider
-// workgroups lost at one token, narrower ones at four, sixteen waves and
-// deeper loads lost everywhere; at one token 16 columns beat 32 by 0.4 us).
+// Eight waves per workgroup, two column blocks loaded ahead; the widest of
+// 64, 32 or 16 output columns per workgroup that still gives at least
+// kSumMinGroups workgroups (about two per CU): at hidden 7168 that is 16
+// columns at one token, 32 at two and three, 64 from four.  Measured at
+// hidden 7168, intermediate 2048, top-8: 30.2 / 90.8 us per layer at 1 / 4
+// tokens, against 34.9 / 99.7 us for the route + FC1 + FC2 + combine chain;
+// wider workgroups lost at one token, narrower ones at four, sixteen waves
+// and deeper loads lost everywhere; by this rule, against 64 columns from two
+// tokens and 32 at one: 42.0 -> 40.5 us at two tokens, 61.3 -> 59.1 us at
+// three, 25.8 -> 25.7 us at one, and 20.9 -> 19.3 us at one token of the
+// K3 shapes (hidden 3584: 16 columns, 224 workgroups).
+constexpr int kSumMinGroups = 448;
 constexpr int kSumWaves = 8;
 constexpr int kSumP = 2;
 
@@ -104,8 +110,9 @@ hipError_t launch_sum(const FcArgs& a, const float* weights, int32_t T, int32_t 
 hipError_t launch_fc2_sum_per_route(const FcArgs& a, const float* weights, int32_t T, int32_t H, float* acc,
                                     uint16_t* out, hipStream_t stream) {
   // every row-block count is a multiple of 8 (H a multiple of 128)
-  if (T == 1) return launch_sum<1>(a, weights, T, H, acc, out, stream);
-  return launch_sum<4>(a, weights, T, H, acc, out, stream);
+  if (a.mat.nb / 4 * T >= kSumMinGroups) return launch_sum<4>(a, weights, T, H, acc, out, stream);
+  if (a.mat.nb / 2 * T >= kSumMinGroups) return launch_sum<2>(a, weights, T, H, acc, out, stream);
+  return launch_sum<1>(a, weights, T, H, acc, out, stream);
 }
 
 }  // namespace moe
