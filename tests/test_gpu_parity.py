@@ -501,9 +501,10 @@ def test_two_k_ranges_per_wave_give_the_same_bits(act):
     blocks in four ranges of 12, 12, 8, 8 (one wave takes 0-24 with a split at
     12, the other 24-40 with a split at 32), intermediate 1536 gives FC2 12
     blocks in ranges of 8 and 4 (one wave, split at 8).  The rows of 40
-    tokens (two ranges per FC1 and FC2 wave), 16 (one per FC1 wave), 4 (the
-    per-route path for bf16) and 1 agree bit for bit, and three of the rows
-    match the oracle."""
+    tokens (two ranges per FC1 and FC2 wave), 16 (one per FC1 wave), 4, 3, 2
+    and 1 (the per-route path for bf16, its FC2 workgroups 32 columns wide at
+    four and three tokens, 16 at two and one) agree bit for bit, and three of
+    the rows match the oracle."""
     case = W.make_case("ranges", W.LayerShape(40, 5120, 1536, 48, 60, 8), 91, routing="uniform",
                        invalid_frac=0.1, act=act)
     say(f"two K ranges per wave ({act}): 40 tokens, hidden 5120, intermediate 1536, 48 experts")
@@ -521,7 +522,7 @@ def test_two_k_ranges_per_wave_give_the_same_bits(act):
 
     out40, acc40 = run(40)
     check_layer(case, out40, acc40, tokens=[0, 21, 39], plan=plan)   # before h is overwritten
-    for n in (16, 4, 1):
+    for n in (16, 4, 3, 2, 1):
         out_n, acc_n = run(n)
         np.testing.assert_array_equal(G.bf16_bits(out_n), G.bf16_bits(out40)[:n])
         np.testing.assert_array_equal(acc_n.cpu().numpy().view(np.uint32), acc40.cpu().numpy()[:n].view(np.uint32))
